@@ -1,0 +1,177 @@
+"""Python binding of libfp32gemm.so (fp32 SGEMM / small-M SGEMV for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the shared library.  The functions with the C names (``sgemm``,
+``sgemv``, ``fp32gemm_*``) take the same arguments as the C entry points,
+with device pointers given as ints or torch tensors, and return the C return
+code.  ``gemm`` is a torch-tensor convenience wrapper that raises on error.
+
+PyTorch serves only for device memory and streams.  The library must be built
+(``python -m fp32_gemm_06_amd.build``); there is no fallback of any kind when
+it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp32gemm.so")
+_lib = None
+
+KIND_SGEMM = 0
+KIND_SGEMV = 1
+ERR_CONFIG = -100
+
+_GEMM_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+
+# Every symbol include/fp32gemm.h declares.
+EXPORTS = ("sgemm", "sgemv", "fp32gemm_strerror", "fp32gemm_num_configs",
+           "fp32gemm_config_name", "fp32gemm_select_config",
+           "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
+
+
+class Fp32GemmError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"fp32gemm error {code}: {strerror(code)}")
+        self.code = code
+
+
+def lib():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m fp32_gemm_06_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sgemm.argtypes = _GEMM_ARGTYPES
+        L.sgemm.restype = ctypes.c_int
+        L.sgemv.argtypes = _GEMM_ARGTYPES
+        L.sgemv.restype = ctypes.c_int
+        L.fp32gemm_strerror.argtypes = [ctypes.c_int]
+        L.fp32gemm_strerror.restype = ctypes.c_char_p
+        L.fp32gemm_num_configs.argtypes = [ctypes.c_int]
+        L.fp32gemm_num_configs.restype = ctypes.c_int
+        L.fp32gemm_config_name.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.fp32gemm_config_name.restype = ctypes.c_char_p
+        L.fp32gemm_select_config.argtypes = [ctypes.c_int] * 4
+        L.fp32gemm_select_config.restype = ctypes.c_int
+        L.fp32gemm_sgemm_with_config.argtypes = [ctypes.c_int] + _GEMM_ARGTYPES
+        L.fp32gemm_sgemm_with_config.restype = ctypes.c_int
+        L.fp32gemm_sgemv_with_config.argtypes = [ctypes.c_int] + _GEMM_ARGTYPES
+        L.fp32gemm_sgemv_with_config.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _addr(x):
+    """Device address of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """C <- alpha A B + beta C (row-major fp32); returns the C return code."""
+    return lib().sgemm(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                       _stream(stream))
+
+
+def sgemv(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """Same operation for 1 <= M <= 8 (decode shape); returns the C return code."""
+    return lib().sgemv(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                       _stream(stream))
+
+
+def fp32gemm_sgemm_with_config(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                               stream=None) -> int:
+    return lib().fp32gemm_sgemm_with_config(cfg, M, N, K, alpha, _addr(A), lda, _addr(B), ldb,
+                                            beta, _addr(C), ldc, _stream(stream))
+
+
+def fp32gemm_sgemv_with_config(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                               stream=None) -> int:
+    return lib().fp32gemm_sgemv_with_config(cfg, M, N, K, alpha, _addr(A), lda, _addr(B), ldb,
+                                            beta, _addr(C), ldc, _stream(stream))
+
+
+def fp32gemm_strerror(code: int) -> str:
+    return lib().fp32gemm_strerror(code).decode()
+
+
+strerror = fp32gemm_strerror
+
+
+def fp32gemm_num_configs(kind: int) -> int:
+    return lib().fp32gemm_num_configs(kind)
+
+
+def fp32gemm_config_name(kind: int, cfg: int):
+    s = lib().fp32gemm_config_name(kind, cfg)
+    return None if s is None else s.decode()
+
+
+def fp32gemm_select_config(kind: int, M: int, N: int, K: int) -> int:
+    return lib().fp32gemm_select_config(kind, M, N, K)
+
+
+def config_names(kind: int):
+    return [fp32gemm_config_name(kind, i) for i in range(fp32gemm_num_configs(kind))]
+
+
+def _ld(t, name):
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    r, c = t.shape
+    if c > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    return t.stride(0) if r > 1 else max(1, c)
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, config: int | None = None,
+         stream=None):
+    """Torch wrapper: returns C = alpha A @ B + beta C (C allocated when None).
+
+    ``config`` forces a configuration of the SGEMM family (``sgemv`` family
+    when ``A`` has at most 8 rows and ``config`` is given as ("gemv", id)).
+    """
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {A.shape} @ {B.shape}")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
+    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
+    args = (M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc, stream)
+    if config is None:
+        rc = sgemm(*args)
+    elif isinstance(config, tuple) and config[0] == "gemv":
+        rc = fp32gemm_sgemv_with_config(config[1], *args)
+    else:
+        rc = fp32gemm_sgemm_with_config(int(config), *args)
+    if rc != 0:
+        raise Fp32GemmError(rc)
+    return C

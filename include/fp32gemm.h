@@ -1,0 +1,112 @@
+/*
+ * fp32gemm — single-precision GEMM and small-M GEMV for AMD MI355X (gfx950).
+ *
+ * C ABI of libfp32gemm.so.  Plain pointers and sizes only; no HIP or torch
+ * header is needed to call it (the stream is an opaque pointer that is
+ * ABI-identical to hipStream_t).
+ *
+ * The operation is the one defined on the page "GPU GEMM 优化完全拆解（一）：
+ * 从朴素 Kernel 到共享内存分块", section "什么是 GEMM" (A is M x K, B is K x N,
+ * C is M x N, alpha and beta scalars, C <- alpha * A B + beta * C), with the
+ * row-major element update of the naive kernel in "CUDA 矩阵乘法优化：从朴素
+ * Kernel 到接近 cuBLAS", section "1. Kernel 1: 朴素实现".  The small-M
+ * product is the decode-phase matrix-vector shape of the first page's
+ * section "LLM 推理本质上是 GEMM 的串联" (M = batch, usually 1 to 8).
+ *
+ * Conventions shared by every entry point:
+ *  - Layout: row-major fp32.  Element (i, k) of A is A[i * lda + k], element
+ *    (k, j) of B is B[k * ldb + j], element (i, j) of C is C[i * ldc + j].
+ *  - Memory: A, B and C are device pointers (hipMalloc / torch CUDA tensors)
+ *    owned by the caller.  The library keeps no reference after the call's
+ *    kernels finish.  C must not overlap A or B.
+ *  - Arithmetic: fp32 throughout (fp32 MFMA or fp32 FMA); no conversion to a
+ *    narrower format.  The order of the k-sum is unspecified, so results may
+ *    differ from a sequential loop by rounding.  Repeated calls with the same
+ *    arguments and configuration give bit-identical results (no atomics on
+ *    floats).
+ *  - Reads: when beta == 0, C is not read (NaN in C does not propagate).
+ *    When alpha == 0 or K == 0, A and B are not read (they may be NULL) and
+ *    C <- beta * C.  When M == 0 or N == 0 the call does nothing.
+ *  - Alignment: any 4-byte alignment is accepted.  The 128-bit load path is
+ *    used when A and B are 16-byte aligned and K, N, lda and ldb are
+ *    multiples of 4; otherwise a 32-bit load path computes the same result.
+ *  - Asynchrony: work is enqueued on `stream` (NULL = the null stream) and
+ *    the call returns without synchronising.
+ *  - Return value: 0 on success; -p when argument p (1-based, in the order of
+ *    sgemm's parameter list) is invalid; FP32GEMM_ERR_CONFIG for an unknown
+ *    configuration id; a positive hipError_t value when a HIP call or kernel
+ *    launch fails.  Nothing is enqueued when a negative code is returned.
+ *  - Threads: every entry point is reentrant.  Calls on different streams may
+ *    run concurrently (each stream gets its own GEMV workspace).
+ */
+#ifndef FP32GEMM_H
+#define FP32GEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *fp32gemm_stream_t;
+
+#define FP32GEMM_OK 0
+#define FP32GEMM_ERR_CONFIG (-100)
+
+/*
+ * C[M x N] <- alpha * A[M x K] . B[K x N] + beta * C.
+ * Argument checks: M, N, K >= 0; lda >= max(1, K); ldb >= max(1, N);
+ * ldc >= max(1, N); A and B non-NULL when alpha != 0 and K > 0; C non-NULL
+ * when M > 0 and N > 0.  M <= 8 is routed to the GEMV kernel (sgemv); larger
+ * M runs the LDS-tiled fp32 MFMA kernel with the tile configuration that the
+ * per-shape table selects for (M, N, K).
+ */
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+          const float *B, int ldb, float beta, float *C, int ldc,
+          fp32gemm_stream_t stream);
+
+/*
+ * The same operation for 1 <= M <= 8 (the decode shape: X = A is M x K, the
+ * weight W = B is K x N, Y = C is M x N).  Bandwidth-bound: B is streamed
+ * once with 128-bit loads, K is split across workgroups and the partial sums
+ * are reduced in a fixed order (deterministic).  The split uses a workspace
+ * that the library allocates once per (device, stream) on first use and
+ * keeps until process exit; calls on one stream are ordered by the stream.
+ * Returns -1 when M is outside 1..8.
+ */
+int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
+          const float *B, int ldb, float beta, float *C, int ldc,
+          fp32gemm_stream_t stream);
+
+/* Human-readable text for a return code (static storage, never NULL). */
+const char *fp32gemm_strerror(int code);
+
+/*
+ * Tuning and testing hooks.  kind 0 = the SGEMM kernel family, kind 1 = the
+ * GEMV family.  Configurations are numbered 0 .. fp32gemm_num_configs(kind)-1
+ * and named by fp32gemm_config_name (NULL for an unknown id).
+ */
+int fp32gemm_num_configs(int kind);
+const char *fp32gemm_config_name(int kind, int cfg);
+
+/* The configuration sgemm()/sgemv() would pick for this shape (kind as above). */
+int fp32gemm_select_config(int kind, int M, int N, int K);
+
+/*
+ * sgemm / sgemv with a forced configuration (cfg = -1 picks as the plain
+ * entry point does).  Same contract and codes as sgemm; the M <= 8 routing
+ * is not applied: fp32gemm_sgemm_with_config always runs the MFMA kernel and
+ * fp32gemm_sgemv_with_config always the GEMV kernel (M must be 1..8).
+ */
+int fp32gemm_sgemm_with_config(int cfg, int M, int N, int K, float alpha,
+                               const float *A, int lda, const float *B,
+                               int ldb, float beta, float *C, int ldc,
+                               fp32gemm_stream_t stream);
+int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha,
+                               const float *A, int lda, const float *B,
+                               int ldb, float beta, float *C, int ldc,
+                               fp32gemm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32GEMM_H */
