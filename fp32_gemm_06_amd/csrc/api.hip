@@ -3,10 +3,6 @@
 // The host-side launch mirrors the pages' launch step (grid over C tiles,
 // asynchronous launch that returns at once; "CUDA 矩阵乘法优化", section
 // "1. Kernel 1: 朴素实现"), with the grid shape taken from the chosen tile.
-#include <map>
-#include <mutex>
-#include <utility>
-
 #include "../../include/fp32gemm.h"
 #include "common.h"
 
@@ -50,43 +46,6 @@ int quick_return(const GemmArgs &a, hipStream_t s, int *rc) {
   return 0;
 }
 
-// GEMV workspace, one per (device, stream), allocated on first use.
-struct Workspace {
-  float *buf = nullptr;
-  unsigned *counters = nullptr;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
-hipError_t workspace_for(hipStream_t s, Workspace *out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  auto it = g_ws.find({dev, s});
-  if (it != g_ws.end()) {
-    *out = it->second;
-    return hipSuccess;
-  }
-  Workspace w;
-  e = hipMalloc(&w.buf, gemv_work_floats() * sizeof(float));
-  if (e != hipSuccess) return e;
-  e = hipMalloc(&w.counters, (size_t)gemv_max_counters() * sizeof(unsigned));
-  if (e != hipSuccess) {
-    (void)hipFree(w.buf);
-    return e;
-  }
-  e = hipMemset(w.counters, 0, (size_t)gemv_max_counters() * sizeof(unsigned));
-  if (e != hipSuccess) {
-    (void)hipFree(w.buf);
-    (void)hipFree(w.counters);
-    return e;
-  }
-  g_ws[{dev, s}] = w;
-  *out = w;
-  return hipSuccess;
-}
-
 int run_gemm(int cfg, const GemmArgs &a, hipStream_t s) {
   int ntiles = 0;
   const GemmConfig *tiles = gemm_configs(&ntiles);
@@ -101,10 +60,7 @@ int run_gemv(int cfg, const GemmArgs &a, hipStream_t s) {
   const GemvConfig *cfgs = gemv_configs(&n);
   if (cfg < 0) cfg = select_gemv_config(a.M, a.N, a.K);
   if (cfg >= n) return FP32GEMM_ERR_CONFIG;
-  Workspace w;
-  const hipError_t e = workspace_for(s, &w);
-  if (e != hipSuccess) return (int)e;
-  return (int)launch_gemv_with(cfgs[cfg], a, w.buf, w.counters, s);
+  return (int)cfgs[cfg].launch(a, s);
 }
 
 GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const float *B,

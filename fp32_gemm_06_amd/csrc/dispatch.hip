@@ -99,7 +99,9 @@ int select_gemv_config(int M, int N, int K) {
       const int id = find_gemv(e.name);
       if (id >= 0) return id;
     }
-  return find_gemv("u8_wg1024") >= 0 ? find_gemv("u8_wg1024") : 0;
+  // Narrow column blocks keep enough workgroups in flight unless N is huge.
+  const int id = find_gemv(N >= 65536 ? "c64_w16_u8" : "c16_w8_u8");
+  return id >= 0 ? id : 0;
 }
 
 }  // namespace fp32gemm

@@ -1,52 +1,62 @@
 // Small-M product Y[M x N] <- alpha X[M x K] W[K x N] + beta Y, 1 <= M <= 8.
 //
 // This is the decode-phase shape of "GPU GEMM 优化完全拆解（一）", section
-// "LLM 推理本质上是 GEMM 的串联": M is the batch, and the work is bound by
-// the bandwidth needed to stream W once, not by arithmetic.  The pages give
-// no kernel for it; the design applies their coalescing rule ("GPU 基础原理",
-// section "4.3 合并加载"; 128-bit loads as in "CUDA 矩阵乘法优化", section
-// "7. Kernel 6") and the split-K reduction that the worklog credits for
-// small problems ("CUDA 矩阵乘法优化", section "10. cuBLAS 领先的性能差异",
-// split-K and a reduction step), with a deterministic reduction order.
+// "LLM 推理本质上是 GEMM 的串联": M is the batch, and the time is the time to
+// stream W once from HBM.  The pages give no kernel for it; the design keeps
+// their coalescing rule ("GPU 基础原理", section "4.3 合并加载"), 128-bit
+// loads ("CUDA 矩阵乘法优化", section "7. Kernel 6") and a K split with a
+// reduction step ("10. cuBLAS 领先的性能差异"), but the reduction never
+// leaves the workgroup:
 //
-// Mapping.  A workgroup owns a column block of 64 lanes x 4 columns (one
-// 1 KB row segment of W per wave instruction) and a range of R rows of W
-// (the K split).  Its waves take interleaved chunks of U rows; each lane
-// keeps U 128-bit loads in flight and M x 4 fp32 accumulators.  X values are
-// the same for the whole wave and come in through scalar loads.  The waves'
-// partial sums are added in LDS in wave order; with one split the workgroup
-// writes Y directly, otherwise it writes its partial sums to a workspace and
-// the last workgroup of the column block to finish (counted with an atomic
-// counter) adds the splits in split order, applies alpha / beta and resets
-// the counter.  No float atomics: the result does not depend on timing.
+//  * a workgroup owns CBW columns of W over the whole of K, so it needs no
+//    other workgroup's partial sums (a cross-workgroup reduction would need
+//    an agent-scope release/acquire, which on this GPU writes back and
+//    invalidates the XCD's whole L2 per workgroup);
+//  * with CBW = 16 and N = 4096 that is 256 workgroups, one per CU; each row
+//    segment is 64 bytes.  The two column blocks that share a 128-byte line
+//    run on the same XCD (so the line is fetched once into that L2), and the
+//    line pairs an XCD owns are spread across the row: a workgroup's stream
+//    of rows keeps one address offset modulo the row stride, and with a
+//    power-of-two stride (N = 4096: 16 KB) a contiguous window of columns
+//    per XCD concentrates its traffic on few memory channels;
+//  * lanes are grouped LPR to a row (one float4 each); a wave instruction
+//    reads RPI = 64 / LPR rows; lane group g of wave w takes U consecutive
+//    rows per pass, so its X values are U consecutive floats per batch row;
+//  * every lane keeps U loads of W in flight and M x 4 fp32 accumulators;
+//  * partial sums are added across the lane groups of a wave with a fixed
+//    butterfly, then across waves in LDS in wave order: the summation order
+//    does not depend on timing, so results are bit-reproducible.
 #include "common.h"
 
 namespace fp32gemm {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-
-template <int MR, bool VEC, int U>
-__global__ void __launch_bounds__(kThreads)
-sgemv_kernel(GemmArgs a, int rows_per_split, float *work, unsigned *counters) {
-  constexpr int VW = VEC ? 4 : 1;   // columns per lane
-  constexpr int CB = 64 * VW;       // columns per workgroup
-  __shared__ float red[kWaves][MR][CB];
-  __shared__ int is_last;
+template <int MR, bool VEC, bool XVEC, int CBW, int NW, int U>
+__global__ void __launch_bounds__(NW * 64)
+sgemv_kernel(GemmArgs a) {
+  constexpr int VW = VEC ? 4 : 1;     // columns per lane
+  constexpr int LPR = CBW / VW;       // lanes per row
+  constexpr int RPI = 64 / LPR;       // rows per wave instruction
+  constexpr int ROWS = NW * RPI * U;  // rows per workgroup pass
+  static_assert(64 % LPR == 0 && CBW % VW == 0, "lane mapping");
+  static_assert(!XVEC || U % 4 == 0, "X is read in float4 pieces");
+  __shared__ float red[NW][MR][CBW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cb = blockIdx.x, sp = blockIdx.y, splits = gridDim.y;
-  const int n0 = cb * CB;
-  const int kb = sp * rows_per_split;
-  const int ke = min(a.K, kb + rows_per_split);
+  const int g = lane / LPR;           // row group inside the wave
+  const int cl = (lane % LPR) * VW;   // first column of this lane in the block
 
-  // Column validity is fixed per lane: a lane outside N gets the rejected
-  // offset and loads zeros.
-  const int col = lane * VW;
-  const bool col_ok = n0 + col < a.N;
+  // Column block: workgroups go to the XCDs round-robin by id (XCD = id % 8);
+  // blocks 2j and 2j+1 go to XCD j % 8.  Ids past the last full group of 16
+  // keep their own number.
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int cb = bid < (G & ~15)
+                     ? 2 * (8 * ((bid >> 3) >> 1) + (bid & 7)) + ((bid >> 3) & 1)
+                     : bid;
+  const int n0 = cb * CBW;
+  const bool col_ok = n0 + cl < a.N;  // VEC: N % 4 == 0, so the float4 is whole
 
   float acc[MR][VW];
 #pragma unroll
@@ -54,128 +64,83 @@ sgemv_kernel(GemmArgs a, int rows_per_split, float *work, unsigned *counters) {
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[m][e] = 0.0f;
 
-  const size_t ldb = (size_t)a.ldb;
-  for (int k = kb + wave * U; k < ke; k += kWaves * U) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B + (size_t)k * ldb + n0);
-    if (k + U <= ke) {
-      float w[U][VW];
+  const int ldb = a.ldb, lda = a.lda;
+  for (int k0 = 0; k0 < a.K; k0 += ROWS) {
+    // this lane's rows: k0 + wave * RPI * U + g * U + u, u < U.  The wave's
+    // first row goes into the buffer base so byte offsets stay below 2^31.
+    const int kw = k0 + wave * RPI * U;
+    const int r0 = g * U;
+    const int nrows = a.K - kw - r0;  // rows of this lane still inside K
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)kw * ldb + n0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + kw);
+    float w[U][VW];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t off = col_ok ? (uint32_t)(u * a.ldb + col) * 4u : kOob;
-        if constexpr (VEC) {
-          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const bool ok = col_ok && u < nrows;
+      const uint32_t off = ok ? (uint32_t)((r0 + u) * ldb + cl) * 4u : kOob;
+      if constexpr (VEC) {
+        const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[u][e] = v[e];
-        } else {
-          w[u][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        for (int e = 0; e < 4; ++e) w[u][e] = v[e];
+      } else {
+        w[u][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float x[U];
+      if constexpr (XVEC) {
+        // rows kw + r0 + u start on a multiple of 4 and K % 4 == 0, so each
+        // float4 of X is entirely inside or entirely outside K
+#pragma unroll
+        for (int q = 0; q < U / 4; ++q) {
+          const uint32_t off = 4 * q < nrows ? (uint32_t)(m * lda + r0 + 4 * q) * 4u : kOob;
+          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t off = u < nrows ? (uint32_t)(m * lda + r0 + u) * 4u : kOob;
+          x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          const float x = a.A[(size_t)m * a.lda + k + u];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) acc[m][e] += x * w[u][e];
-        }
-    } else {
-      for (int u = 0; u < ke - k; ++u) {
-        const uint32_t off = col_ok ? (uint32_t)(u * a.ldb + col) * 4u : kOob;
-        float w[VW];
-        if constexpr (VEC) {
-          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = v[e];
-        } else {
-          w[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          const float x = a.A[(size_t)m * a.lda + k + u];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) acc[m][e] += x * w[e];
-        }
-      }
+        for (int e = 0; e < VW; ++e) acc[m][e] += x[u] * w[u][e];
     }
   }
 
-  // Sum the waves' partial results in wave order.
+  // Butterfly over the row groups of the wave (lane bits above the column bits).
 #pragma unroll
-  for (int m = 0; m < MR; ++m)
+  for (int s = LPR; s < 64; s <<= 1)
 #pragma unroll
-    for (int e = 0; e < VW; ++e) red[wave][m][col + e] = acc[m][e];
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[m][e] += __shfl_xor(acc[m][e], s, 64);
+  if (g == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) red[wave][m][cl + e] = acc[m][e];
+  }
   __syncthreads();
 
-  constexpr int OUTS = MR * CB;                      // outputs of this workgroup
-  constexpr int PER = (OUTS + kThreads - 1) / kThreads;
-  float part[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int o = tid + p * kThreads;
-    float s = 0.0f;
-    if (o < OUTS) {
-      const int m = o / CB, c = o % CB;
-      s = red[0][m][c];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) s += red[w][m][c];
-    }
-    part[p] = s;
-  }
-
+  // Waves in wave order, then the alpha/beta update.
   const float alpha = a.alpha, beta = a.beta;
-  auto finish = [&](int o, float s) {
-    const int m = o / CB, c = o % CB;
-    if (n0 + c >= a.N) return;
+  for (int o = tid; o < MR * CBW; o += NW * 64) {
+    const int m = o / CBW, c = o % CBW;
+    if (n0 + c >= a.N) continue;
+    float s = red[0][m][c];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) s += red[w2][m][c];
     float *y = a.C + (size_t)m * a.ldc + n0 + c;
     float out = alpha * s;
     if (beta != 0.0f) out += beta * *y;
     *y = out;
-  };
-
-  if (splits == 1) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int o = tid + p * kThreads;
-      if (o < OUTS) finish(o, part[p]);
-    }
-    return;
   }
-
-  // Publish this split's partial sums, then count arrivals for the column block.
-  const size_t N = (size_t)a.N;
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int o = tid + p * kThreads;
-    if (o < OUTS) {
-      const int m = o / CB, c = o % CB;
-      if (n0 + c < a.N) work[((size_t)sp * MR + m) * N + n0 + c] = part[p];
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&counters[cb], 1u);
-    is_last = (prev == (unsigned)(splits - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // Last arrival: add the splits in split order.
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int o = tid + p * kThreads;
-    if (o < OUTS) {
-      const int m = o / CB, c = o % CB;
-      if (n0 + c < a.N) {
-        const float *src = work + (size_t)m * N + n0 + c;
-        float s = src[0];
-        for (int q = 1; q < splits; ++q) s += src[(size_t)q * MR * N];
-        finish(o, s);
-      }
-    }
-  }
-  if (tid == 0) counters[cb] = 0u;  // ready for the next call on this stream
 }
 
 // C <- beta * C; beta == 0 stores zeros without reading C.
@@ -188,75 +153,55 @@ __global__ void __launch_bounds__(256) scale_kernel(float *C, int M, int N, int 
   }
 }
 
-template <int MR, bool VEC, int U>
-void launch_one(dim3 grid, const GemmArgs &a, int R, float *work, unsigned *counters, hipStream_t s) {
-  hipLaunchKernelGGL((sgemv_kernel<MR, VEC, U>), grid, dim3(kThreads), 0, s, a, R, work, counters);
+template <bool VEC, bool XVEC, int CBW, int NW, int U>
+hipError_t launch_cfg(const GemmArgs &a, hipStream_t s) {
+  const long long blocks = ((long long)a.N + CBW - 1) / CBW;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(NW * 64);
+  switch (a.M) {
+#define FP32GEMM_GEMV_CASE(MR)                                                                  \
+  case MR:                                                                                      \
+    hipLaunchKernelGGL((sgemv_kernel<MR, VEC, XVEC, CBW, NW, U>), grid, block, 0, s, a); break;
+    FP32GEMM_GEMV_CASE(1)
+    FP32GEMM_GEMV_CASE(2)
+    FP32GEMM_GEMV_CASE(3)
+    FP32GEMM_GEMV_CASE(4)
+    FP32GEMM_GEMV_CASE(5)
+    FP32GEMM_GEMV_CASE(6)
+    FP32GEMM_GEMV_CASE(7)
+    FP32GEMM_GEMV_CASE(8)
+#undef FP32GEMM_GEMV_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
-template <bool VEC, int U>
-void launch_m(dim3 grid, const GemmArgs &a, int R, float *work, unsigned *counters, hipStream_t s) {
-  switch (a.M) {
-    case 1: launch_one<1, VEC, U>(grid, a, R, work, counters, s); break;
-    case 2: launch_one<2, VEC, U>(grid, a, R, work, counters, s); break;
-    case 3: launch_one<3, VEC, U>(grid, a, R, work, counters, s); break;
-    case 4: launch_one<4, VEC, U>(grid, a, R, work, counters, s); break;
-    case 5: launch_one<5, VEC, U>(grid, a, R, work, counters, s); break;
-    case 6: launch_one<6, VEC, U>(grid, a, R, work, counters, s); break;
-    case 7: launch_one<7, VEC, U>(grid, a, R, work, counters, s); break;
-    default: launch_one<8, VEC, U>(grid, a, R, work, counters, s); break;
-  }
+// 128-bit loads of W need B 16-byte aligned and N, ldb multiples of 4; of X,
+// A 16-byte aligned and K, lda multiples of 4.
+template <int CBW, int NW, int U>
+hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
+  const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
+  const bool xvec = ((uintptr_t)a.A % 16 == 0) && a.K % 4 == 0 && a.lda % 4 == 0;
+  if (vec)
+    return xvec ? launch_cfg<true, true, CBW, NW, U>(a, s) : launch_cfg<true, false, CBW, NW, U>(a, s);
+  return xvec ? launch_cfg<false, true, CBW, NW, U>(a, s) : launch_cfg<false, false, CBW, NW, U>(a, s);
 }
 
 }  // namespace
 
 const GemvConfig *gemv_configs(int *count) {
   static const GemvConfig table[] = {
-      {"u8_wg512", kWaves, 8, 512},    {"u8_wg1024", kWaves, 8, 1024},
-      {"u8_wg2048", kWaves, 8, 2048},  {"u16_wg512", kWaves, 16, 512},
-      {"u16_wg1024", kWaves, 16, 1024}, {"u16_wg2048", kWaves, 16, 2048},
-      {"u4_wg1024", kWaves, 4, 1024},  {"u4_wg2048", kWaves, 4, 2048},
+      {"c16_w8_u8", 16, 8, 8, &launch_gemv<16, 8, 8>},
+      {"c16_w8_u4", 16, 8, 4, &launch_gemv<16, 8, 4>},
+      {"c16_w16_u4", 16, 16, 4, &launch_gemv<16, 16, 4>},
+      {"c16_w4_u8", 16, 4, 8, &launch_gemv<16, 4, 8>},
+      {"c16_w8_u16", 16, 8, 16, &launch_gemv<16, 8, 16>},
+      {"c16_w16_u8", 16, 16, 8, &launch_gemv<16, 16, 8>},
+      {"c32_w8_u8", 32, 8, 8, &launch_gemv<32, 8, 8>},
+      {"c64_w16_u8", 64, 16, 8, &launch_gemv<64, 16, 8>},
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
-}
-
-// Workspace the K split may use, per (device, stream).
-size_t gemv_work_floats() { return (size_t)4 << 20; }  // 16 MB
-int gemv_max_counters() { return 65536; }
-
-hipError_t launch_gemv_with(const GemvConfig &cfg, const GemmArgs &a, float *work,
-                            unsigned *counters, hipStream_t s) {
-  const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
-  const int cbw = vec ? 256 : 64;
-  const long long cbs = ((long long)a.N + cbw - 1) / cbw;
-  if (cbs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int U = cfg.unroll;
-  // Split K so that about target_wgs workgroups run; each split is a
-  // multiple of U rows; the workspace and counter limits cap the split.
-  long long splits = (cfg.target_wgs + cbs - 1) / cbs;
-  const long long max_by_rows = ((long long)a.K + U - 1) / U;
-  if (splits > max_by_rows) splits = max_by_rows;
-  if (splits > 65535) splits = 65535;
-  if (work == nullptr || counters == nullptr || cbs > gemv_max_counters() ||
-      splits * a.M * (long long)a.N > (long long)gemv_work_floats())
-    splits = 1;
-  if (splits < 1) splits = 1;
-  long long R = ((a.K + splits - 1) / splits + U - 1) / U * U;
-  if (R < U) R = U;
-  splits = (a.K + R - 1) / R;
-  if (splits < 1) splits = 1;
-  const dim3 grid((unsigned)cbs, (unsigned)splits);
-  const int Ri = (int)R;
-  if (vec) {
-    if (U == 4) launch_m<true, 4>(grid, a, Ri, work, counters, s);
-    else if (U == 8) launch_m<true, 8>(grid, a, Ri, work, counters, s);
-    else launch_m<true, 16>(grid, a, Ri, work, counters, s);
-  } else {
-    if (U == 4) launch_m<false, 4>(grid, a, Ri, work, counters, s);
-    else if (U == 8) launch_m<false, 8>(grid, a, Ri, work, counters, s);
-    else launch_m<false, 16>(grid, a, Ri, work, counters, s);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_scale(const GemmArgs &a, hipStream_t s) {

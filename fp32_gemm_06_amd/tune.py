@@ -1,0 +1,160 @@
+"""Tile-configuration sweep and per-shape table generator.
+
+The pages pick block and thread-tile sizes by timing every legal setting on
+the target GPU and keeping the fastest ("CUDA 矩阵乘法优化：从朴素 Kernel 到接
+近 cuBLAS", section "8. Kernel 9: 参数自动调优"); the best settings differ
+from GPU to GPU.  This sweep does the same on MI355X over the library's
+configurations (tile shape x tile-ordering group for SGEMM; unroll x
+workgroup target for GEMV), through the C ABI with a forced configuration.
+
+    python -m fp32_gemm_06_amd.tune --out results.jsonl     # on the GPU
+    python -m fp32_gemm_06_amd.tune --table results.jsonl   # writes csrc/tune_table.inc
+
+Results are appended one JSON line per (shape, configuration), so an
+interrupted sweep resumes by skipping the keys already present.  Legality
+(LDS <= 160 KB per workgroup, <= 512 registers per lane) is enforced at
+compile time for every configuration in the library.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TABLE = os.path.join(HERE, "csrc", "tune_table.inc")
+
+# (family, M, N, K, alpha, beta)
+SHAPES = [
+    ("gemm", 128, 128, 128, 1.0, 0.5),
+    ("gemm", 4092, 4092, 4092, 1.0, 0.0),
+    ("gemm", 4096, 4096, 4096, 0.5, 1.0),
+    ("gemm", 2048, 11008, 4096, 1.0, 0.0),
+    ("gemv", 1, 4096, 4096, 1.0, 0.0),
+    ("gemv", 4, 4096, 4096, 1.0, 0.0),
+    ("gemv", 8, 4096, 4096, 1.0, 0.0),
+]
+
+
+def _key(fam, M, N, K, name):
+    return f"{fam}:{M}x{N}x{K}:{name}"
+
+
+def sweep(out_path: str, reps: int, warm: int, only: str | None):
+    import torch
+
+    import fp32_gemm_06_amd as fg
+
+    done = set()
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            for ln in f:
+                if ln.strip():
+                    done.add(json.loads(ln)["key"])
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    with open(out_path, "a") as out:
+        for (fam, M, N, K, alpha, beta) in SHAPES:
+            if only and only != fam:
+                continue
+            kind = fg.KIND_SGEMM if fam == "gemm" else fg.KIND_SGEMV
+            A = torch.randn(M, K, device=dev)
+            nbuf = 8 if fam == "gemv" else 1  # gemv: exceed the Infinity Cache
+            Bs = [torch.randn(K, N, device=dev) for _ in range(nbuf)]
+            C = torch.randn(M, N, device=dev)
+            fn = fg.fp32gemm_sgemm_with_config if fam == "gemm" else fg.fp32gemm_sgemv_with_config
+            auto = fg.fp32gemm_select_config(kind, M, N, K)
+            for cfg in range(fg.fp32gemm_num_configs(kind)):
+                name = fg.fp32gemm_config_name(kind, cfg)
+                key = _key(fam, M, N, K, name)
+                if key in done:
+                    continue
+                n = reps * (4 if fam == "gemv" else 1)
+
+                def call(i):
+                    rc = fn(cfg, M, N, K, alpha, A, K, Bs[i % nbuf], N, beta, C, N, sp)
+                    if rc:
+                        raise fg.Fp32GemmError(rc)
+
+                for i in range(warm):
+                    call(i)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(n):
+                    call(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / n * 1e3
+                rec = {"key": key, "family": fam, "M": M, "N": N, "K": K, "config": name,
+                       "us": round(us, 3), "auto": cfg == auto}
+                if fam == "gemm":
+                    rec["tflops"] = round(2.0 * M * N * K / (us * 1e-6) / 1e12, 3)
+                else:
+                    b = 4 * (M * K + K * N + M * N)
+                    rec["gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+                out.write(json.dumps(rec) + "\n")
+                out.flush()
+                print(json.dumps(rec), flush=True)
+            del A, Bs, C
+            torch.cuda.empty_cache()
+
+
+def best_by_shape(path: str):
+    best = {}
+    with open(path) as f:
+        for ln in f:
+            if not ln.strip():
+                continue
+            r = json.loads(ln)
+            k = (r["family"], r["M"], r["N"], r["K"])
+            if k not in best or r["us"] < best[k]["us"]:
+                best[k] = r
+    return best
+
+
+def write_table(path: str, table: str = TABLE):
+    best = best_by_shape(path)
+    lines = [
+        "// Per-shape configuration table.  Written by fp32_gemm_06_amd/tune.py from a",
+        "// timing sweep on MI355X; entries name a configuration (tile shape and tile",
+        "// ordering group for SGEMM, unroll and workgroup target for GEMV).",
+        "// {M, N, K, \"configuration name\"}",
+        "static const ShapeEntry kGemmTable[] = {",
+    ]
+    for (fam, M, N, K), r in sorted(best.items()):
+        if fam == "gemm":
+            lines.append(f"    {{{M}, {N}, {K}, \"{r['config']}\"}},  // {r['us']} us")
+    lines.append("};")
+    lines.append("static const ShapeEntry kGemvTable[] = {")
+    for (fam, M, N, K), r in sorted(best.items()):
+        if fam == "gemv":
+            lines.append(f"    {{{M}, {N}, {K}, \"{r['config']}\"}},  // {r['us']} us")
+    lines.append("};")
+    with open(table, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return table
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None, help="append sweep results (JSON lines) here")
+    ap.add_argument("--table", default=None, help="write tune_table.inc from these results")
+    ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--warm", type=int, default=5)
+    ap.add_argument("--only", choices=["gemm", "gemv"], default=None)
+    a = ap.parse_args()
+    if a.out:
+        sweep(a.out, a.reps, a.warm, a.only)
+    if a.table:
+        print(write_table(a.table))
+    if not a.out and not a.table:
+        ap.print_help()
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,8 +36,9 @@
  *    sgemm's parameter list) is invalid; FP32GEMM_ERR_CONFIG for an unknown
  *    configuration id; a positive hipError_t value when a HIP call or kernel
  *    launch fails.  Nothing is enqueued when a negative code is returned.
- *  - Threads: every entry point is reentrant.  Calls on different streams may
- *    run concurrently (each stream gets its own GEMV workspace).
+ *  - Threads: every entry point is reentrant and keeps no per-call state;
+ *    calls on different streams may run concurrently.  The library allocates
+ *    no device memory.
  */
 #ifndef FP32GEMM_H
 #define FP32GEMM_H
@@ -65,12 +66,11 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
 
 /*
  * The same operation for 1 <= M <= 8 (the decode shape: X = A is M x K, the
- * weight W = B is K x N, Y = C is M x N).  Bandwidth-bound: B is streamed
- * once with 128-bit loads, K is split across workgroups and the partial sums
- * are reduced in a fixed order (deterministic).  The split uses a workspace
- * that the library allocates once per (device, stream) on first use and
- * keeps until process exit; calls on one stream are ordered by the stream.
- * Returns -1 when M is outside 1..8.
+ * weight W = B is K x N, Y = C is M x N).  Bandwidth-bound: each workgroup
+ * streams a narrow block of W's columns over all of K with 128-bit loads,
+ * its waves split K, and the partial sums are added inside the workgroup in
+ * a fixed order (deterministic, no workspace, no atomics).  Returns -1 when
+ * M is outside 1..8.
  */
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
