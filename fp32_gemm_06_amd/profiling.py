@@ -1,0 +1,160 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m fp32_gemm_06_amd.profiling <run dir> <out prefix> "<command that made it>"
+
+<run dir> holds the CSV output of one kernel-trace run (trace/) and of
+counter runs (pmc*/), each made with ``--output-format csv``.  Writes
+<out prefix>_<kernel>.md summaries and, for the SGEMM and GEMV kernels,
+<out prefix>_<kernel>_traffic.json with HBM bytes per launch.
+
+HBM bytes come from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+scaled by what the same counter reads for a calibration kernel of known
+size in the same run (an elementwise negation that reads and writes
+``bytes_each_way``): scale = known bytes / counted bytes.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "fp32_gemm_06_amd", "csrc")
+KERNELS = {
+    "sgemm_4092": ("sgemm_mfma<", ["sgemm_mfma.hip", "common.h", "tune_table.inc"]),
+    "gemv_m1_4096": ("sgemv_kernel<1,", ["sgemv.hip", "common.h", "tune_table.inc"]),
+}
+CALIB = "neg_kernel"
+CALIB_BYTES = 256 << 20
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_stats(run_dir):
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "trace", "*kernel_stats.csv")):
+        for r in csv.DictReader(open(path)):
+            out[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                              "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    return out
+
+
+def dispatch_durations(run_dir):
+    """{kernel name: [duration us, in dispatch order]} from the kernel trace."""
+    out = defaultdict(list)
+    for path in glob.glob(os.path.join(run_dir, "trace", "*kernel_trace.csv")):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
+            out[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
+def counters(run_dir):
+    """{kernel name: {counter: [values per dispatch]}} over all pmc*/ runs."""
+    agg = defaultdict(lambda: defaultdict(list))
+    for path in glob.glob(os.path.join(run_dir, "pmc*", "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _find(d, key):
+    hits = [k for k in d if key in k.replace(" ", "")]
+    return hits[0] if hits else None
+
+
+def _avg(v):
+    return sum(v) / len(v) if v else float("nan")
+
+
+def summarize(run_dir, prefix, command, timed=(50, 400)):
+    """timed: dispatches of the timed window per kernel (the last ones of the
+    SGEMM / GEMV sequence of the run; earlier ones are warm-up)."""
+    stats = kernel_stats(run_dir)
+    durs = dispatch_durations(run_dir)
+    ctr = counters(run_dir)
+    calib = _find(ctr, CALIB)
+    fetch_scale = write_scale = None
+    if calib:
+        c = ctr[calib]
+        # the largest dispatches of the calibration kernel are the 256 MiB ones
+        if c.get("FETCH_SIZE"):
+            fetch_scale = CALIB_BYTES / (max(c["FETCH_SIZE"]) * 1024.0)
+        if c.get("WRITE_SIZE"):
+            write_scale = CALIB_BYTES / (max(c["WRITE_SIZE"]) * 1024.0)
+    written = []
+    for tag, (needle, files) in KERNELS.items():
+        sk = _find(stats, needle.replace(" ", ""))
+        ck = _find(ctr, needle.replace(" ", ""))
+        if not sk:
+            continue
+        s = stats[sk]
+        lines = [f"# {tag}: rocprofv3 summary", "", f"Kernel: `{sk}`", "",
+                 "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+                 f"Kernel source hash: `{source_hash(files)}`", "",
+                 "| quantity | value |", "|---|---|",
+                 f"| dispatches traced | {s['calls']} |",
+                 f"| average duration | {s['avg_us']:.3f} us |",
+                 f"| min / max duration | {s['min_us']:.3f} / {s['max_us']:.3f} us |"]
+        rec = {"kernel": sk, "source_hash": source_hash(files), "avg_us": s["avg_us"]}
+        d = durs.get(sk, [])
+        want = timed[0] if tag.startswith("sgemm") else timed[1]
+        if d:
+            # the SGEMM's timed steps follow its warm-up; the GEMV's cycled calls
+            # follow 32 warm-up calls and precede the single-buffer calls
+            if tag.startswith("sgemm"):
+                win = d[-want:]
+            else:
+                win = d[32:32 + want]
+            rec["timed_avg_us"] = sum(win) / len(win)
+            lines.append(f"| average over the timed window ({len(win)} dispatches) | "
+                         f"{rec['timed_avg_us']:.3f} us |")
+        if ck:
+            c = ctr[ck]
+            for name in sorted(c):
+                lines.append(f"| {name} (mean per dispatch) | {_avg(c[name]):.6g} |")
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("GRBM_GUI_ACTIVE"):
+                # busy cycles are summed over the 1024 SIMDs, GUI_ACTIVE over the 8 XCDs
+                util = _avg(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024.0 / (_avg(c["GRBM_GUI_ACTIVE"]) / 8.0)
+                lines.append(f"| MFMA busy fraction (busy per SIMD / active cycles per XCD) | {util:.4f} |")
+                rec["mfma_busy_fraction"] = util
+            if c.get("FETCH_SIZE") and fetch_scale:
+                fb = _avg(c["FETCH_SIZE"]) * 1024.0 * fetch_scale
+                lines.append(f"| HBM read bytes per launch (FETCH_SIZE x {fetch_scale:.4f}) | {fb:.6g} |")
+                rec["fetch_bytes"] = fb
+                rec["fetch_scale"] = fetch_scale
+            if c.get("WRITE_SIZE") and write_scale:
+                wb = _avg(c["WRITE_SIZE"]) * 1024.0 * write_scale
+                lines.append(f"| HBM write bytes per launch (WRITE_SIZE x {write_scale:.4f}) | {wb:.6g} |")
+                rec["write_bytes"] = wb
+                rec["write_scale"] = write_scale
+            if "fetch_bytes" in rec and "write_bytes" in rec:
+                rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+        if calib:
+            lines += ["", f"Calibration kernel `{calib[:60]}...` moves {CALIB_BYTES} bytes each way; "
+                          "counter scale = known bytes / counted bytes."]
+        md = f"{prefix}_{tag}.md"
+        with open(md, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(md)
+        if "bytes_per_launch" in rec:
+            js = os.path.join(os.path.dirname(prefix), f"{tag}_traffic.json")
+            with open(js, "w") as f:
+                json.dump(rec, f, indent=1)
+            written.append(js)
+    return written
+
+
+if __name__ == "__main__":
+    for w in summarize(sys.argv[1], sys.argv[2], sys.argv[3]):
+        print(w)

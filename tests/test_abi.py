@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it builds/loads, exports every symbol the
+header declares, and its host-side logic (argument checks, quick returns,
+configuration names and selection) works without a GPU."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp32_gemm_06_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp32gemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fg.LIB_PATH):
+        from fp32_gemm_06_amd import build
+        build.build()
+    return fg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    assert set(names) == set(fg.EXPORTS), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else leaks out of the library as a global function
+    assert exported == set(declared_functions()), exported - set(declared_functions())
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void) {{ return sgemm(0,0,0,1.0f,0,1,0,1,0.0f,0,1,0); }}\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+ARGS = dict(M=4, N=4, K=4, alpha=1.0, A=16, lda=4, B=16, ldb=4, beta=0.0, C=16, ldc=4)
+
+
+def call(fn, **kw):
+    a = dict(ARGS, **kw)
+    return fn(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"], a["ldb"], a["beta"],
+              a["C"], a["ldc"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3),
+    (dict(A=None), -5), (dict(K=8, lda=4), -6), (dict(B=None), -7),
+    (dict(N=8, ldb=4, ldc=8), -8), (dict(C=None), -10), (dict(N=8, ldb=8, ldc=4), -11),
+    (dict(lda=(1 << 20) + 1), -6), (dict(ldb=(1 << 20) + 1), -8), (dict(ldc=(1 << 20) + 1), -11),
+])
+def test_argument_checks_need_no_gpu(lib, kw, code):
+    assert call(fg.sgemm, **kw) == code
+    assert call(fg.sgemv, **kw) == code
+    assert "invalid argument" in fg.strerror(code)
+
+
+def test_quick_returns_need_no_gpu(lib):
+    # M == 0 or N == 0: nothing happens, NULL pointers are fine
+    assert call(fg.sgemm, M=0, A=None, B=None, C=None) == 0
+    assert call(fg.sgemm, N=0, A=None, B=None, C=None, ldb=1, ldc=1) == 0
+    # alpha == 0 and beta == 1: C is left alone, A and B may be NULL
+    assert call(fg.sgemm, alpha=0.0, beta=1.0, A=None, B=None) == 0
+    # K == 0 and beta == 1
+    assert call(fg.sgemm, K=0, lda=1, beta=1.0, A=None, B=None) == 0
+
+
+def test_gemv_batch_range(lib):
+    assert call(fg.sgemv, M=9) == -1
+    assert call(fg.sgemv, M=0) == -1
+    assert fg.fp32gemm_sgemv_with_config(0, 9, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, 0) == -1
+
+
+def test_configs(lib):
+    for kind in (fg.KIND_SGEMM, fg.KIND_SGEMV):
+        n = fg.fp32gemm_num_configs(kind)
+        assert n > 0
+        names = fg.config_names(kind)
+        assert len(set(names)) == n and all(names)
+        assert fg.fp32gemm_config_name(kind, n) is None
+        assert fg.fp32gemm_config_name(kind, -1) is None
+    assert fg.fp32gemm_num_configs(7) == 0
+    assert fg.fp32gemm_select_config(7, 1, 1, 1) == fg.ERR_CONFIG
+    assert fg.fp32gemm_sgemm_with_config(10 ** 6, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, 0) == \
+        fg.ERR_CONFIG
+    assert fg.strerror(fg.ERR_CONFIG) == "unknown configuration id"
+
+
+@pytest.mark.parametrize("shape", [(4092, 4092, 4092), (4096, 4096, 4096), (2048, 11008, 4096),
+                                   (128, 128, 128), (1, 1, 1), (100000, 16, 16)])
+def test_selection_is_a_valid_sgemm_config(lib, shape):
+    cfg = fg.fp32gemm_select_config(fg.KIND_SGEMM, *shape)
+    assert 0 <= cfg < fg.fp32gemm_num_configs(fg.KIND_SGEMM)
+
+
+def test_tuned_shapes_resolve_to_their_table_entries(lib):
+    table = open(os.path.join(ROOT, "fp32_gemm_06_amd", "csrc", "tune_table.inc")).read()
+    gemm_part, gemv_part = table.split("kGemvTable")
+    for fam, part in ((fg.KIND_SGEMM, gemm_part), (fg.KIND_SGEMV, gemv_part)):
+        for M, N, K, name in re.findall(r'\{(\d+), (\d+), (\d+), "([^"]+)"\}', part):
+            cfg = fg.fp32gemm_select_config(fam, int(M), int(N), int(K))
+            assert fg.fp32gemm_config_name(fam, cfg) == name, (M, N, K, name)
