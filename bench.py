@@ -6,7 +6,9 @@ One step is one full sgemm() call on the 4092 x 4092 x 4092 workload
 benchmarks ("CUDA 矩阵乘法优化：从朴素 Kernel 到接近 cuBLAS", table at the top
 of the page).  Inputs are resident in HBM before timing starts; W steps are
 warm-up, then K steps are timed with HIP events on the stream the kernels run
-on, bracketed by device synchronisations.  The decode GEMV (M = 1, K = N =
+on, bracketed by device synchronisations.  The default warm-up (60 steps,
+about 60 ms) covers the clock ramp: the first ~30 dispatches after the GPU
+wakes run slower while the clock rises.  The decode GEMV (M = 1, K = N =
 4096) is timed in the same run, cycling over enough weight copies that each
 call streams its weights from HBM rather than from the 256 MB Infinity Cache.
 
@@ -58,8 +60,8 @@ def stored_traffic(name: str, paths):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=60)
     p.add_argument("--gemv-steps", type=int, default=400)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample (0 disables)")

@@ -25,7 +25,7 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp32_gemm_06_amd", "csrc")
 KERNELS = {
-    "sgemm_4092": ("sgemm_mfma<", ["sgemm_mfma.hip", "common.h", "tune_table.inc"]),
+    "sgemm_4092": ("sgemm_mfma", ["sgemm_mfma.hip", "common.h", "tune_table.inc"]),
     "gemv_m1_4096": ("sgemv_kernel<1,", ["sgemv.hip", "common.h", "tune_table.inc"]),
 }
 CALIB = "neg_kernel"
@@ -77,7 +77,7 @@ def _avg(v):
     return sum(v) / len(v) if v else float("nan")
 
 
-def summarize(run_dir, prefix, command, timed=(50, 400)):
+def summarize(run_dir, prefix, command, timed=(100, 400)):
     """timed: dispatches of the timed window per kernel (the last ones of the
     SGEMM / GEMV sequence of the run; earlier ones are warm-up)."""
     stats = kernel_stats(run_dir)
