@@ -520,9 +520,13 @@ hipError_t launch(const GemmArgs &a, bool vec4, int group_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-#define FP32GEMM_CFG(BM, BN, BK, WM, WN)                                                  \
+// OCC: workgroups per CU of the 128-bit kernel, from its LDS size (160 KB per
+// CU) and register count (512 per SIMD lane, waves spread over 4 SIMDs), as
+// reported by the compiler for gfx950.
+#define FP32GEMM_CFG(BM, BN, BK, WM, WN, OCC)                                             \
   {#BM "x" #BN "x" #BK "_w" #WM "x" #WN, BM, BN, BK, WM, WN, Tile<BM, BN, BK, WM, WN>::NT, \
-   (int)(2 * Dma<Tile<BM, BN, BK, WM, WN>>::STAGE * sizeof(float)), &launch<Tile<BM, BN, BK, WM, WN>>}
+   (int)(2 * Dma<Tile<BM, BN, BK, WM, WN>>::STAGE * sizeof(float)), OCC,                   \
+   &launch<Tile<BM, BN, BK, WM, WN>>}
 
 }  // namespace
 
@@ -530,17 +534,17 @@ hipError_t launch(const GemmArgs &a, bool vec4, int group_m, hipStream_t s) {
 // limits: LDS <= 160 KB per workgroup, at most 512 registers per lane.
 const GemmConfig *gemm_configs(int *count) {
   static const GemmConfig table[] = {
-      FP32GEMM_CFG(256, 256, 32, 128, 64),
-      FP32GEMM_CFG(256, 256, 16, 128, 64),
-      FP32GEMM_CFG(256, 128, 32, 64, 64),
-      FP32GEMM_CFG(128, 256, 32, 64, 64),
-      FP32GEMM_CFG(128, 128, 32, 64, 32),
-      FP32GEMM_CFG(256, 128, 32, 128, 64),
-      FP32GEMM_CFG(256, 128, 16, 128, 64),
-      FP32GEMM_CFG(128, 256, 32, 64, 128),
-      FP32GEMM_CFG(128, 128, 32, 64, 64),
-      FP32GEMM_CFG(128, 128, 16, 64, 64),
-      FP32GEMM_CFG(64, 64, 32, 32, 32),
+      FP32GEMM_CFG(256, 256, 32, 128, 64, 1),  // 131 KB LDS
+      FP32GEMM_CFG(256, 256, 16, 128, 64, 1),  // 192 VGPRs x 2 waves/SIMD per workgroup
+      FP32GEMM_CFG(256, 128, 32, 64, 64, 1),   // 99 KB LDS
+      FP32GEMM_CFG(128, 256, 32, 64, 64, 1),   // 99 KB LDS
+      FP32GEMM_CFG(128, 128, 32, 64, 32, 2),   // 66 KB LDS
+      FP32GEMM_CFG(256, 128, 32, 128, 64, 1),  // 99 KB LDS
+      FP32GEMM_CFG(256, 128, 16, 128, 64, 1),  // 292 VGPRs: one wave per SIMD
+      FP32GEMM_CFG(128, 256, 32, 64, 128, 1),  // 99 KB LDS
+      FP32GEMM_CFG(128, 128, 32, 64, 64, 2),   // 66 KB LDS
+      FP32GEMM_CFG(128, 128, 16, 64, 64, 3),   // 33 KB LDS, 164 VGPRs: 3 waves/SIMD
+      FP32GEMM_CFG(64, 64, 32, 32, 32, 4),     // 33 KB LDS
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

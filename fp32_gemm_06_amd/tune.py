@@ -25,12 +25,26 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "csrc", "tune_table.inc")
 
-# (family, M, N, K, alpha, beta)
+# (family, M, N, K, alpha, beta): the benchmark workloads, the square sizes of
+# the pages' size comparison, and transformer projection shapes (prefill
+# M = tokens; N, K = 4096 / 11008 hidden and FFN widths).
 SHAPES = [
     ("gemm", 128, 128, 128, 1.0, 0.5),
     ("gemm", 4092, 4092, 4092, 1.0, 0.0),
     ("gemm", 4096, 4096, 4096, 0.5, 1.0),
     ("gemm", 2048, 11008, 4096, 1.0, 0.0),
+    ("gemm", 256, 256, 256, 1.0, 0.0),
+    ("gemm", 512, 512, 512, 1.0, 0.0),
+    ("gemm", 768, 768, 768, 1.0, 0.0),
+    ("gemm", 1024, 1024, 1024, 1.0, 0.0),
+    ("gemm", 1536, 1536, 1536, 1.0, 0.0),
+    ("gemm", 2048, 2048, 2048, 1.0, 0.0),
+    ("gemm", 3072, 3072, 3072, 1.0, 0.0),
+    ("gemm", 8192, 8192, 8192, 1.0, 0.0),
+    ("gemm", 2048, 4096, 4096, 1.0, 0.0),
+    ("gemm", 2048, 4096, 11008, 1.0, 0.0),
+    ("gemm", 512, 11008, 4096, 1.0, 0.0),
+    ("gemm", 512, 4096, 4096, 1.0, 0.0),
     ("gemv", 1, 4096, 4096, 1.0, 0.0),
     ("gemv", 4, 4096, 4096, 1.0, 0.0),
     ("gemv", 8, 4096, 4096, 1.0, 0.0),
