@@ -366,40 +366,32 @@ sgemm_mfma_dma(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   const int ktail = a.K - (nk - 1) * BK;
 
   // This lane's source offsets (bytes from the slice's base) per DMA
-  // instruction, with the row / column masks applied, and the k index (inside
-  // the slice) that decides whether the chunk exists in a short last slice.
+  // instruction; kvalid masks the k range of the slice.
   uint32_t offa[D::NIA], offb[D::NIB];
-  int ka[D::NIA], kb[D::NIB];
+  auto set_offsets = [&](int kvalid) {
 #pragma unroll
-  for (int q = 0; q < D::NIA; ++q) {
-    const int r = (wave * D::NIA + q) * D::RPA + lane / D::CPA;
-    ka[q] = 4 * ((lane % D::CPA) ^ a_swizzle<BK>(r));
-    offa[q] = r < rows ? (uint32_t)(r * a.lda + ka[q]) * 4u : kOob;
-  }
+    for (int q = 0; q < D::NIA; ++q) {
+      const int r = (wave * D::NIA + q) * D::RPA + lane / D::CPA;
+      const int k = 4 * ((lane % D::CPA) ^ a_swizzle<BK>(r));
+      offa[q] = (r < rows && k < kvalid) ? (uint32_t)(r * a.lda + k) * 4u : kOob;
+    }
 #pragma unroll
-  for (int q = 0; q < D::NIB; ++q) {
-    kb[q] = (wave * D::NIB + q) * D::RPB + lane / D::CPB;
-    const int c = (lane % D::CPB) * 4;
-    offb[q] = c < cols ? (uint32_t)(kb[q] * a.ldb + c) * 4u : kOob;
-  }
-  // K slices run in a rotated order that differs between XCDs: with a
-  // power-of-two row stride the workgroups' concurrent A reads would
-  // otherwise all sit at one offset modulo the stride (few memory
-  // channels).  Workgroups on one XCD keep a common order, so the tiles that
-  // share A or B panels in that XCD's L2 still read them at the same time.
-  const int rot = ((bid & 7) * nk) >> 3;
-  auto slice_of = [&](int i) { return i + rot < nk ? i + rot : i + rot - nk; };
-  auto dma_slice = [&](float *buf, int ks) {
-    const int kvalid = ks == nk - 1 ? ktail : BK;
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + (size_t)m0 * a.lda + (size_t)ks * BK);
-    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(a.B + (size_t)ks * BK * a.ldb + n0);
+    for (int q = 0; q < D::NIB; ++q) {
+      const int k = (wave * D::NIB + q) * D::RPB + lane / D::CPB;
+      const int c = (lane % D::CPB) * 4;
+      offb[q] = (k < kvalid && c < cols) ? (uint32_t)(k * a.ldb + c) * 4u : kOob;
+    }
+  };
+  auto dma_slice = [&](float *buf, int kt) {
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A + (size_t)m0 * a.lda + (size_t)kt * BK);
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(a.B + (size_t)kt * BK * a.ldb + n0);
 #pragma unroll
     for (int q = 0; q < D::NIA; ++q)
-      dma16(rs_a, buf + (wave * D::NIA + q) * 256, ka[q] < kvalid ? offa[q] : kOob);
+      dma16(rs_a, buf + (wave * D::NIA + q) * 256, offa[q]);
 #pragma unroll
     for (int q = 0; q < D::NIB; ++q) {
       const int rb = (wave * D::NIB + q) * D::RPB;
-      dma16(rs_b, buf + D::A_ST + rb * BN + (rb >= BK / 2 ? 32 : 0), kb[q] < kvalid ? offb[q] : kOob);
+      dma16(rs_b, buf + D::A_ST + rb * BN + (rb >= BK / 2 ? 32 : 0), offb[q]);
     }
   };
 
@@ -444,7 +436,10 @@ sgemm_mfma_dma(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   // read one group ahead; the last group is multiplied after the barrier.
   auto slice = [&](const float *cur, float *nxt, int kt) {
     const bool more = kt + 1 < nk;
-    if (more) dma_slice(nxt, slice_of(kt + 1));
+    if (more) {
+      if (kt + 2 == nk) set_offsets(ktail);
+      dma_slice(nxt, kt + 1);
+    }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       Frag &fc = (g & 1) ? f1 : f0;
@@ -461,7 +456,8 @@ sgemm_mfma_dma(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
-  dma_slice(lds, slice_of(0));
+  set_offsets(nk == 1 ? ktail : BK);
+  dma_slice(lds, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   read_frag(lds, 0, f0);
