@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_06_amd", "csrc", f)
-                  for f in ("sgemm_mfma.hip", "common.h", "tune_table.inc")]
+                  for f in ("sgemm_kernel.h", "sgemm_nn.hip", "common.h", "tune_table.inc")]
 GEMV_SOURCES = [os.path.join(ROOT, "fp32_gemm_06_amd", "csrc", f)
                 for f in ("sgemv.hip", "common.h", "tune_table.inc")]
 

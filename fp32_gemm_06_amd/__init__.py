@@ -27,9 +27,19 @@ _GEMM_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                   ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
 
+OP_N = 0
+OP_T = 1
+
+_EX_ARGTYPES = [ctypes.c_int, ctypes.c_int] + _GEMM_ARGTYPES
+_BATCHED_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                     ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong,
+                     ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float,
+                     ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                     ctypes.c_void_p]
+
 # Every symbol include/fp32gemm.h declares.
-EXPORTS = ("sgemm", "sgemv", "fp32gemm_strerror", "fp32gemm_num_configs",
-           "fp32gemm_config_name", "fp32gemm_select_config",
+EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "fp32gemm_strerror",
+           "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
            "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
 
 
@@ -50,6 +60,10 @@ def lib():
         L.sgemm.restype = ctypes.c_int
         L.sgemv.argtypes = _GEMM_ARGTYPES
         L.sgemv.restype = ctypes.c_int
+        L.sgemm_ex.argtypes = _EX_ARGTYPES
+        L.sgemm_ex.restype = ctypes.c_int
+        L.sgemm_strided_batched.argtypes = _BATCHED_ARGTYPES
+        L.sgemm_strided_batched.restype = ctypes.c_int
         L.fp32gemm_strerror.argtypes = [ctypes.c_int]
         L.fp32gemm_strerror.restype = ctypes.c_char_p
         L.fp32gemm_num_configs.argtypes = [ctypes.c_int]
@@ -94,6 +108,20 @@ def sgemv(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
     """Same operation for 1 <= M <= 8 (decode shape); returns the C return code."""
     return lib().sgemv(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                        _stream(stream))
+
+
+def sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """C <- alpha op(A) op(B) + beta C with op = identity (0) or transpose (1)."""
+    return lib().sgemm_ex(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                          _addr(C), ldc, _stream(stream))
+
+
+def sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                          beta, C, ldc, strideC, batch_count, stream=None) -> int:
+    """batch_count products with element strides between the entries."""
+    return lib().sgemm_strided_batched(transA, transB, M, N, K, alpha, _addr(A), lda, strideA,
+                                       _addr(B), ldb, strideB, beta, _addr(C), ldc, strideC,
+                                       batch_count, _stream(stream))
 
 
 def fp32gemm_sgemm_with_config(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

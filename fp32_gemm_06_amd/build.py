@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
-SOURCES = ["api.hip", "dispatch.hip", "sgemm_mfma.hip", "sgemv.hip"]
+SOURCES = ["api.hip", "dispatch.hip", "sgemm_configs.hip", "sgemm_nn.hip", "sgemm_nt.hip",
+           "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -16,26 +16,42 @@ constexpr int kMaxLd = 1 << 20;
 
 int imax(int a, int b) { return a > b ? a : b; }
 
-int check_args(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
-               int ldb, float beta, float *C, int ldc) {
-  (void)beta;
-  if (M < 0) return -1;
-  if (N < 0) return -2;
-  if (K < 0) return -3;
-  if (lda < imax(1, K) || lda > kMaxLd) return -6;
-  if (ldb < imax(1, N) || ldb > kMaxLd) return -8;
-  if (ldc < imax(1, N) || ldc > kMaxLd) return -11;
-  const bool reads_ab = alpha != 0.0f && K > 0 && M > 0 && N > 0;
-  if (reads_ab && A == nullptr) return -5;
-  if (reads_ab && B == nullptr) return -7;
-  if (M > 0 && N > 0 && C == nullptr) return -10;
+// 1-based positions of the arguments in a routine's parameter list (0 when
+// the routine has no such argument), for BLAS-style -p error codes.
+struct Pos {
+  int ta, tb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch;
+};
+constexpr Pos kPosSgemm = {0, 0, 1, 2, 3, 5, 6, 0, 7, 8, 0, 10, 11, 0, 0};
+constexpr Pos kPosSgemmEx = {1, 2, 3, 4, 5, 7, 8, 0, 9, 10, 0, 12, 13, 0, 0};
+constexpr Pos kPosBatched = {1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14, 15, 16, 17};
+
+int check_args(const Pos &p, int ta, int tb, const GemmArgs &a) {
+  if (ta != 0 && ta != 1) return -p.ta;
+  if (tb != 0 && tb != 1) return -p.tb;
+  if (a.M < 0) return -p.M;
+  if (a.N < 0) return -p.N;
+  if (a.K < 0) return -p.K;
+  if (a.lda < imax(1, ta ? a.M : a.K) || a.lda > kMaxLd) return -p.lda;
+  if (p.sA && a.sA < 0) return -p.sA;
+  if (a.ldb < imax(1, tb ? a.K : a.N) || a.ldb > kMaxLd) return -p.ldb;
+  if (p.sB && a.sB < 0) return -p.sB;
+  if (a.ldc < imax(1, a.N) || a.ldc > kMaxLd) return -p.ldc;
+  if (p.batch && a.batch < 0) return -p.batch;
+  // batch entries of C must not overlap
+  if (p.sC && a.batch > 1 && a.M > 0 && a.N > 0 && a.sC < (long long)(a.M - 1) * a.ldc + a.N)
+    return -p.sC;
+  const bool work = a.M > 0 && a.N > 0 && a.batch > 0;
+  const bool reads_ab = work && a.alpha != 0.0f && a.K > 0;
+  if (reads_ab && a.A == nullptr) return -p.A;
+  if (reads_ab && a.B == nullptr) return -p.B;
+  if (work && a.C == nullptr) return -p.C;
   return 0;
 }
 
-// Quick returns shared by both families.  Returns 1 when the call is done
+// Quick returns shared by every routine.  Returns 1 when the call is done
 // (result code in *rc), 0 when the main kernel has to run.
 int quick_return(const GemmArgs &a, hipStream_t s, int *rc) {
-  if (a.M == 0 || a.N == 0) {
+  if (a.M == 0 || a.N == 0 || a.batch == 0) {
     *rc = 0;
     return 1;
   }
@@ -46,13 +62,13 @@ int quick_return(const GemmArgs &a, hipStream_t s, int *rc) {
   return 0;
 }
 
-int run_gemm(int cfg, const GemmArgs &a, hipStream_t s) {
+int run_gemm(int cfg, int ta, int tb, const GemmArgs &a, hipStream_t s) {
   int ntiles = 0;
   const GemmConfig *tiles = gemm_configs(&ntiles);
   if (cfg < 0) cfg = select_gemm_config(a.M, a.N, a.K);
   if (cfg >= ntiles * kNumGroups) return FP32GEMM_ERR_CONFIG;
   const GemmConfig &c = tiles[cfg / kNumGroups];
-  return (int)c.launch(a, vec4_ok(a), kGroups[cfg % kNumGroups], s);
+  return (int)c.launch[2 * ta + tb](a, vec4_ok(a, ta, tb), kGroups[cfg % kNumGroups], s);
 }
 
 int run_gemv(int cfg, const GemmArgs &a, hipStream_t s) {
@@ -70,6 +86,8 @@ GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const f
   a.alpha = alpha; a.beta = beta;
   a.A = A; a.B = B; a.C = C;
   a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+  a.sA = a.sB = a.sC = 0;
+  a.batch = 1;
   return a;
 }
 
@@ -80,44 +98,65 @@ extern "C" {
 
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, fp32gemm_stream_t stream) {
-  int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc) return rc;
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemm, 0, 0, a);
+  if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
   if (M <= 8) return run_gemv(-1, a, s);
-  return run_gemm(-1, a, s);
+  return run_gemm(-1, 0, 0, a, s);
 }
 
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, fp32gemm_stream_t stream) {
   if (M < 1 || M > 8) return -1;
-  int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc) return rc;
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemm, 0, 0, a);
+  if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
   return run_gemv(-1, a, s);
 }
 
+int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, fp32gemm_stream_t stream) {
+  const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemmEx, transA, transB, a);
+  if (rc) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quick_return(a, s, &rc)) return rc;
+  if (M <= 8 && !transA && !transB) return run_gemv(-1, a, s);
+  return run_gemm(-1, transA, transB, a, s);
+}
+
+int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alpha,
+                          const float *A, int lda, long long strideA, const float *B, int ldb,
+                          long long strideB, float beta, float *C, int ldc, long long strideC,
+                          int batch_count, fp32gemm_stream_t stream) {
+  GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  a.sA = strideA;
+  a.sB = strideB;
+  a.sC = strideC;
+  a.batch = batch_count;
+  int rc = check_args(kPosBatched, transA, transB, a);
+  if (rc) return rc;
+  if (batch_count > 65535) return -kPosBatched.batch;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quick_return(a, s, &rc)) return rc;
+  return run_gemm(-1, transA, transB, a, s);
+}
+
 const char *fp32gemm_strerror(int code) {
-  switch (code) {
-    case 0: return "success";
-    case -1: return "invalid argument 1 (M)";
-    case -2: return "invalid argument 2 (N)";
-    case -3: return "invalid argument 3 (K)";
-    case -4: return "invalid argument 4 (alpha)";
-    case -5: return "invalid argument 5 (A is NULL but referenced)";
-    case -6: return "invalid argument 6 (lda < max(1,K) or lda > 2^20)";
-    case -7: return "invalid argument 7 (B is NULL but referenced)";
-    case -8: return "invalid argument 8 (ldb < max(1,N) or ldb > 2^20)";
-    case -9: return "invalid argument 9 (beta)";
-    case -10: return "invalid argument 10 (C is NULL)";
-    case -11: return "invalid argument 11 (ldc < max(1,N) or ldc > 2^20)";
-    case -12: return "invalid argument 12 (stream)";
-    case FP32GEMM_ERR_CONFIG: return "unknown configuration id";
-    default: break;
-  }
+  static const char *const bad[] = {
+      "invalid argument 1",  "invalid argument 2",  "invalid argument 3",
+      "invalid argument 4",  "invalid argument 5",  "invalid argument 6",
+      "invalid argument 7",  "invalid argument 8",  "invalid argument 9",
+      "invalid argument 10", "invalid argument 11", "invalid argument 12",
+      "invalid argument 13", "invalid argument 14", "invalid argument 15",
+      "invalid argument 16", "invalid argument 17", "invalid argument 18"};
+  if (code == 0) return "success";
+  if (code == FP32GEMM_ERR_CONFIG) return "unknown configuration id";
+  if (code < 0 && code >= -18) return bad[-code - 1];
   if (code > 0) return hipGetErrorString(static_cast<hipError_t>(code));
   return "unknown error code";
 }
@@ -152,12 +191,12 @@ int fp32gemm_sgemm_with_config(int cfg, int M, int N, int K, float alpha, const 
                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
                                fp32gemm_stream_t stream) {
   if (cfg < -1 || cfg >= num_gemm_config_ids()) return FP32GEMM_ERR_CONFIG;
-  int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc) return rc;
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemm, 0, 0, a);
+  if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  return run_gemm(cfg, a, s);
+  return run_gemm(cfg, 0, 0, a, s);
 }
 
 int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha, const float *A,
@@ -165,9 +204,9 @@ int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha, const 
                                fp32gemm_stream_t stream) {
   if (cfg < -1 || cfg >= fp32gemm_num_configs(1)) return FP32GEMM_ERR_CONFIG;
   if (M < 1 || M > 8) return -1;
-  int rc = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (rc) return rc;
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemm, 0, 0, a);
+  if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
   return run_gemv(cfg, a, s);

@@ -1,0 +1,417 @@
+// SGEMM C <- alpha op(A) op(B) + beta C on gfx950 with the fp32 matrix cores.
+// Included by sgemm_nn.hip, sgemm_nt.hip, sgemm_tn.hip and sgemm_tt.hip, which
+// instantiate it for one operand-layout combination each.
+//
+// The structure follows the tiling the pages build up step by step, mapped
+// onto CDNA4:
+//  * a workgroup owns a BM x BN tile of C and walks K in slices of BK
+//    ("GPU 基础原理", section "4.2 分块": the sum over k regrouped by tiles);
+//  * each K slice of both operands is staged in LDS, loaded with 128-bit
+//    coalesced reads ("GPU 基础原理", section "4.3 合并加载"; "CUDA 矩阵乘法
+//    优化", section "7. Kernel 6: 向量化访存优化"), here with the
+//    buffer_load ... lds DMA path that writes LDS without VGPR staging;
+//  * LDS layouts are free of bank conflicts ("GPU GEMM 优化完全拆解（一）",
+//    sections "32 个 bank" and "两种解法：Padding 与线性化"): k-contiguous
+//    tiles use an XOR swizzle of 16-byte chunks, mn-contiguous tiles a gap
+//    between their two k-halves;
+//  * each 64-lane wave owns a WM x WN sub-tile of 32 x 32 blocks, the CDNA4
+//    counterpart of warp tiling with per-thread register blocks ("CUDA 矩阵乘
+//    法优化", sections "6. Kernel 5" and "9. Kernel 10: 线程束级分块"); the
+//    outer product becomes v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate);
+//  * slice k+1 is fetched while the matrix cores work on slice k, with two
+//    LDS buffers and one barrier per slice (double buffering, "11. 探索未尽与
+//    总结"; the two-barrier rule of "GPU GEMM 优化完全拆解（一）", section
+//    "分块的思想");
+//  * tiles that overhang M, N or K are zero-filled by buffer loads whose
+//    out-of-range offsets read zero, and stores outside C are dropped the same
+//    way ("GPU 基础原理", section "最后一个考虑：分块的量化"), so interior and
+//    edge tiles run one instruction stream.
+//
+// Operand layouts.  op(A) is M x K and op(B) is K x N.  An operand is
+// k-contiguous (KC) when its storage rows run along k: A as given, or B when
+// op(B) = B^T (B stored N x K).  It is mn-contiguous (MC) when its rows run
+// along m or n: A when op(A) = A^T (A stored K x M), or B as given.
+//
+// K order inside a slice.  For v_mfma_f32_32x32x2_f32 lane l supplies
+// A[l % 32][k] and B[k][l % 32] with k = l / 32 of the instruction's pair.
+// Any bijection between (step, lane half) and the BK values of k gives the
+// same sum, so lane half h takes k = h * BK/2 + step.  A KC operand then has
+// a lane's values for four consecutive steps next to each other in LDS (one
+// ds_read_b128); an MC operand has the 32 lanes of a half reading 32
+// consecutive floats of one k-row (one ds_read_b32 per step).
+#pragma once
+
+#include "common.h"
+
+namespace fp32gemm {
+namespace {
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_N = BN / WN;
+  static constexpr int WAVES = (BM / WM) * WAVES_N;
+  static constexpr int NT = WAVES * 64;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
+  static_assert(BK == 16 || BK == 32, "K slice of 16 or 32");
+};
+
+// Chunk swizzle of row r of a KC tile (float4 chunks of a BK-float row).
+// Checked exhaustively to keep ds_read_b128 of 32 consecutive rows at one
+// chunk conflict-free for 8-lane/32-bank and 16-lane/64-bank service.
+template <int BK>
+__device__ __forceinline__ int kc_swizzle(int r) {
+  if constexpr (BK == 32) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// One operand tile: `E` rows or columns along m/n (BM for A, BN for B) by BK
+// along k, loaded by `WAVES` waves in whole 1 KB DMA instructions.
+template <bool KC, int E, int BK, int WAVES>
+struct Operand {
+  // LDS floats of the tile
+  static constexpr int FLOATS = KC ? E * BK : BK * E + 32;
+  // DMA instructions per wave per slice (one instruction = 64 lanes x 16 bytes)
+  static constexpr int NI = E * BK / 256 / WAVES;
+  static_assert(E * BK % (256 * WAVES) == 0, "whole DMA instructions per wave");
+  // KC: chunks per row, rows per instruction; MC: chunks per k-row, k-rows per instruction
+  static constexpr int CP = KC ? BK / 4 : E / 4;
+  static constexpr int RP = 64 / CP;
+  static_assert(64 % CP == 0, "rows per instruction");
+  static_assert(KC || (BK / 2) % RP == 0, "an MC instruction stays inside one k-half");
+
+  // LDS float offset where instruction `inst` writes its 1 KB
+  __device__ __forceinline__ static int dst(int inst) {
+    if constexpr (KC) return inst * 256;
+    else {
+      const int k = inst * RP;
+      return k * E + (k >= BK / 2 ? 32 : 0);
+    }
+  }
+  // Source element (row along storage, column along storage) of the first of
+  // the 4 floats this lane moves in instruction `inst`.  KC: (e, k); MC: (k, e).
+  __device__ __forceinline__ static void src(int inst, int lane, int &row, int &col) {
+    if constexpr (KC) {
+      row = inst * RP + lane / CP;                          // along m / n
+      col = 4 * ((lane % CP) ^ kc_swizzle<BK>(row));        // along k
+    } else {
+      row = inst * RP + lane / CP;                          // along k
+      col = (lane % CP) * 4;                                // along m / n
+    }
+  }
+};
+
+// The kernel: one BM x BN tile of C (of batch entry blockIdx.y) per workgroup.
+// DMA = 128-bit loads straight into LDS; otherwise 32-bit loads staged in
+// registers and written to the same LDS positions (any alignment).
+template <class T, bool TRANS_A, bool TRANS_B, bool DMA>
+__global__ void __launch_bounds__(T::NT)
+sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, WAVES = T::WAVES;
+  constexpr bool KCA = !TRANS_A;  // A as given is k-contiguous
+  constexpr bool KCB = TRANS_B;   // B^T storage is k-contiguous
+  using OA = Operand<KCA, BM, BK, WAVES>;
+  using OB = Operand<KCB, BN, BK, WAVES>;
+  constexpr int STAGE = OA::FLOATS + OB::FLOATS;
+  __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+
+  // ---- batch and C tile (XCD-aware order) ---------------------------------
+  // Workgroups are handed to the 8 XCDs round-robin by id; renumber them so
+  // that each XCD receives a contiguous range of logical ids, then walk the
+  // tiles in strips of group_m tile-rows so that the tiles an XCD runs
+  // together share A and B panels in its L2.
+  const long long bz = blockIdx.y;
+  const float *Ag = a.A + bz * a.sA;
+  const float *Bg = a.B + bz * a.sB;
+  float *Cg = a.C + bz * a.sC;
+  const int G = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, per = G >> 3, extra = G & 7;
+  const int lid = xcd * per + min(xcd, extra) + (bid >> 3);
+  const int width = group_m * tiles_n;
+  const int grp = lid / width;
+  const int first_m = grp * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int within = lid - grp * width;
+  const int m0 = (first_m + within % gsz) * BM;
+  const int n0 = (within / gsz) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  const int rows = a.M - m0;  // valid rows of this tile (may exceed BM)
+  const int cols = a.N - n0;
+  const int nk = (a.K + BK - 1) / BK;
+  const int ktail = a.K - (nk - 1) * BK;  // valid k in the last slice, 1..BK
+
+  // Source offset (bytes from the slice's base) of the first of this lane's
+  // 4 floats per instruction, or kOob when the lane's storage row lies
+  // outside the matrix; plus that element's storage column.  On the DMA path
+  // the 4 floats are all valid or all invalid (K and the m/n extent are
+  // multiples of 4 there), so the column check is folded in as well; the
+  // staged path checks each of the 4 floats when it loads them.
+  uint32_t offa[OA::NI], offb[OB::NI];
+  int cola[OA::NI], colb[OB::NI];
+  auto set_offsets = [&](int kvalid) {
+#pragma unroll
+    for (int q = 0; q < OA::NI; ++q) {
+      int row, col;
+      OA::src(wave * OA::NI + q, lane, row, col);
+      // KC: row = m, col = k.  MC: row = k, col = m.
+      const bool row_ok = KCA ? row < rows : row < kvalid;
+      const bool col_ok = KCA ? col < kvalid : col < rows;
+      offa[q] = (row_ok && (col_ok || !DMA)) ? (uint32_t)(row * a.lda + col) * 4u : kOob;
+      cola[q] = col;
+    }
+#pragma unroll
+    for (int q = 0; q < OB::NI; ++q) {
+      int row, col;
+      OB::src(wave * OB::NI + q, lane, row, col);
+      // KC: row = n, col = k.  MC: row = k, col = n.
+      const bool row_ok = KCB ? row < cols : row < kvalid;
+      const bool col_ok = KCB ? col < kvalid : col < cols;
+      offb[q] = (row_ok && (col_ok || !DMA)) ? (uint32_t)(row * a.ldb + col) * 4u : kOob;
+      colb[q] = col;
+    }
+  };
+
+  // Slice bases: the tile origin moved to K slice ks.
+  auto base_a = [&](int ks) -> const float * {
+    return KCA ? Ag + (size_t)m0 * a.lda + (size_t)ks * BK
+               : Ag + (size_t)ks * BK * a.lda + m0;
+  };
+  auto base_b = [&](int ks) -> const float * {
+    return KCB ? Bg + (size_t)n0 * a.ldb + (size_t)ks * BK
+               : Bg + (size_t)ks * BK * a.ldb + n0;
+  };
+
+  // Staged path: registers between the global loads and the LDS writes.
+  floatx4 sa[DMA ? 1 : OA::NI], sb[DMA ? 1 : OB::NI];
+  (void)sa;
+  (void)sb;
+
+  // Start moving slice ks into LDS buffer `buf` (DMA) or into registers.
+  auto fetch = [&](float *buf, int ks) {
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(base_a(ks));
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(base_b(ks));
+    if constexpr (DMA) {
+#pragma unroll
+      for (int q = 0; q < OA::NI; ++q) dma16(rs_a, buf + OA::dst(wave * OA::NI + q), offa[q]);
+#pragma unroll
+      for (int q = 0; q < OB::NI; ++q)
+        dma16(rs_b, buf + OA::FLOATS + OB::dst(wave * OB::NI + q), offb[q]);
+    } else {
+      (void)buf;
+      const int kvalid = ks == nk - 1 ? ktail : BK;
+      // a float is loaded when its storage column is inside the matrix
+      // (the row check is already in the base offset)
+      const int alim = KCA ? kvalid : rows, blim = KCB ? kvalid : cols;
+#pragma unroll
+      for (int q = 0; q < OA::NI; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = cola[q] + e < alim ? offa[q] + 4u * e : kOob;
+          sa[q][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_a, off, 0, 0));
+        }
+#pragma unroll
+      for (int q = 0; q < OB::NI; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = colb[q] + e < blim ? offb[q] + 4u * e : kOob;
+          sb[q][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_b, off, 0, 0));
+        }
+    }
+  };
+  // Staged path: write the registers where the DMA would have put them.
+  auto commit = [&](float *buf) {
+    if constexpr (!DMA) {
+#pragma unroll
+      for (int q = 0; q < OA::NI; ++q)
+        *reinterpret_cast<floatx4 *>(buf + OA::dst(wave * OA::NI + q) + 4 * lane) = sa[q];
+#pragma unroll
+      for (int q = 0; q < OB::NI; ++q)
+        *reinterpret_cast<floatx4 *>(buf + OA::FLOATS + OB::dst(wave * OB::NI + q) + 4 * lane) = sb[q];
+    } else {
+      (void)buf;
+    }
+  };
+
+  floatx16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = floatx16{};
+
+  // Operand fragments of one group of four MFMA steps: per 32-wide block,
+  // this lane's four k values (k = half * BK/2 + 4g + step).
+  struct Frag {
+    float a[T::TM][4];
+    float b[T::TN][4];
+  };
+  const int ar = wm * T::WM + l32;  // this lane's row of block 0 along m
+  const int br = wn * T::WN + l32;  // ... along n
+  const int asw = kc_swizzle<BK>(ar), bsw = kc_swizzle<BK>(br);  // same for every 32-block
+  auto read_frag = [&](const float *buf, int g, Frag &f) {
+    const float *As = buf;
+    const float *Bs = buf + OA::FLOATS;
+    if constexpr (KCA) {
+      const float *pa = As + ar * BK + 4 * ((half * (BK / 8) + g) ^ asw);
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(pa + i * 32 * BK);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) f.a[i][st] = v[st];
+      }
+    } else {
+      const float *pa = As + (half * (BK / 2) + 4 * g) * BM + half * 32 + ar;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) f.a[i][st] = pa[st * BM + i * 32];
+    }
+    if constexpr (KCB) {
+      const float *pb = Bs + br * BK + 4 * ((half * (BK / 8) + g) ^ bsw);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(pb + j * 32 * BK);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) f.b[j][st] = v[st];
+      }
+    } else {
+      const float *pb = Bs + (half * (BK / 2) + 4 * g) * BN + half * 32 + br;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) f.b[j][st] = pb[st * BN + j * 32];
+    }
+  };
+  auto mma = [&](const Frag &f) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][st], f.b[j][st], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- main loop: one barrier per K slice ---------------------------------
+  // The fetch of slice k+1 starts at the top of slice k, into the LDS buffer
+  // the last barrier freed (staged path: into registers, written to that
+  // buffer just before the barrier).  Fragments are read one group of four
+  // MFMA steps ahead; the last group's MFMAs run after the barrier, so they
+  // cover the first LDS reads of the next slice.
+  constexpr int NG = BK / 8;
+  static_assert(NG % 2 == 0, "fragment double buffering needs an even group count");
+  Frag f0, f1;
+  auto slice = [&](const float *cur, float *nxt, int kt) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      if (kt + 2 == nk) set_offsets(ktail);
+      fetch(nxt, kt + 1);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      Frag &fc = (g & 1) ? f1 : f0;
+      Frag &fn = (g & 1) ? f0 : f1;
+      if (g + 1 < NG) {
+        read_frag(cur, g + 1, fn);
+        mma(fc);
+      } else {
+        if (more) commit(nxt);
+        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+        __syncthreads();
+        if (more) read_frag(nxt, 0, fn);
+        mma(fc);
+      }
+    }
+  };
+
+  set_offsets(nk == 1 ? ktail : BK);
+  fetch(lds, 0);
+  commit(lds);
+  if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  read_frag(lds, 0, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int c = kt & 1;
+    slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
+  }
+
+  // ---- epilogue: C = alpha * acc + beta * C -------------------------------
+  // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
+  // column l%32 of its 32 x 32 block.
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(Cg + (size_t)m0 * a.ldc + n0);
+  const float alpha = a.alpha, beta = a.beta;
+  auto c_off = [&](int i, int j, int v) -> uint32_t {
+    const int row = wm * T::WM + i * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+    const int col = wn * T::WN + j * 32 + l32;
+    return (row < rows && col < cols) ? (uint32_t)(row * a.ldc + col) * 4u : kOob;
+  };
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        float c0[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          c0[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_c, c_off(i, j, v), 0, 0));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float out = alpha * acc[i][j][v] + beta * c0[v];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float out = alpha * acc[i][j][v];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
+        }
+  }
+}
+
+// Launch one tile shape for one operand-layout combination.
+template <class T, bool TRANS_A, bool TRANS_B>
+hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
+  const int tm = (a.M + T::BM - 1) / T::BM;
+  const int tn = (a.N + T::BN - 1) / T::BN;
+  const long long G = (long long)tm * tn;
+  if (G > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
+  if (group_m < 1) group_m = 1;
+  const dim3 grid((unsigned)G, (unsigned)a.batch);
+  if (dma)
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, true>), grid, dim3(T::NT), 0, s, a, tm, tn, group_m);
+  else
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, false>), grid, dim3(T::NT), 0, s, a, tm, tn, group_m);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp32gemm
+
+// The tile shapes the tuning sweep chooses from, in configuration order:
+// (BM, BN, BK, WM, WN, workgroups per CU of the 128-bit path).  Each fits the
+// gfx950 limits (LDS <= 160 KB per workgroup, <= 512 registers per lane); the
+// occupancy column comes from the compiler's LDS and register counts.
+#define FP32GEMM_TILES(X)            \
+  X(256, 256, 32, 128, 64, 1)       \
+  X(256, 256, 16, 128, 64, 1)       \
+  X(256, 128, 32, 64, 64, 1)        \
+  X(128, 256, 32, 64, 64, 1)        \
+  X(128, 128, 32, 64, 32, 2)        \
+  X(256, 128, 32, 128, 64, 1)       \
+  X(256, 128, 16, 128, 64, 1)       \
+  X(128, 256, 32, 64, 128, 1)       \
+  X(128, 128, 32, 64, 64, 2)        \
+  X(128, 128, 16, 64, 64, 3)        \
+  X(64, 64, 32, 32, 32, 4)

@@ -1,0 +1,13 @@
+// SGEMM kernels for op(A) = A, op(B) = B^T (see sgemm_kernel.h).
+#include "sgemm_kernel.h"
+
+namespace fp32gemm {
+#define FP32GEMM_LAUNCHER(BM, BN, BK, WM, WN, OCC) &launch<Tile<BM, BN, BK, WM, WN>, false, true>,
+// Fills out[] with this combination's launchers in tile-list order (a host
+// function, so the device pass does not try to emit host function pointers).
+void launchers_nt(GemmLaunchFn *out) {
+  const GemmLaunchFn t[] = {FP32GEMM_TILES(FP32GEMM_LAUNCHER)};
+  for (size_t i = 0; i < sizeof(t) / sizeof(t[0]); ++i) out[i] = t[i];
+}
+#undef FP32GEMM_LAUNCHER
+}  // namespace fp32gemm

@@ -143,12 +143,15 @@ sgemv_kernel(GemmArgs a) {
   }
 }
 
-// C <- beta * C; beta == 0 stores zeros without reading C.
-__global__ void __launch_bounds__(256) scale_kernel(float *C, int M, int N, int ldc, float beta) {
+// C <- beta * C for every batch entry (blockIdx.z); beta == 0 stores zeros
+// without reading C.
+__global__ void __launch_bounds__(256)
+scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= N) return;
+  float *Cz = C + (long long)blockIdx.z * sC;
   for (int i = blockIdx.y; i < M; i += gridDim.y) {
-    float *p = C + (size_t)i * ldc + j;
+    float *p = Cz + (size_t)i * ldc + j;
     *p = (beta == 0.0f) ? 0.0f : beta * *p;
   }
 }
@@ -205,8 +208,9 @@ const GemvConfig *gemv_configs(int *count) {
 }
 
 hipError_t launch_scale(const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 1024 ? a.M : 1024));
-  hipLaunchKernelGGL(scale_kernel, grid, dim3(256), 0, s, a.C, a.M, a.N, a.ldc, a.beta);
+  const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 1024 ? a.M : 1024),
+                  (unsigned)a.batch);
+  hipLaunchKernelGGL(scale_kernel, grid, dim3(256), 0, s, a.C, a.M, a.N, a.ldc, a.sC, a.beta);
   return hipGetLastError();
 }
 

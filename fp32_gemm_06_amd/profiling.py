@@ -25,7 +25,7 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp32_gemm_06_amd", "csrc")
 KERNELS = {
-    "sgemm_4092": ("sgemm_mfma", ["sgemm_mfma.hip", "common.h", "tune_table.inc"]),
+    "sgemm_4092": ("sgemm_kernel", ["sgemm_kernel.h", "sgemm_nn.hip", "common.h", "tune_table.inc"]),
     "gemv_m1_4096": ("sgemv_kernel<1,", ["sgemv.hip", "common.h", "tune_table.inc"]),
 }
 CALIB = "neg_kernel"

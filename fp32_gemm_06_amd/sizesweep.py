@@ -22,6 +22,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", required=True)
     ap.add_argument("--sizes", type=int, nargs="*", default=SIZES)
+    ap.add_argument("--ops", nargs="*", default=["nn"], choices=["nn", "nt", "tn", "tt"],
+                    help="operand layouts: n = as given, t = stored transposed")
     a = ap.parse_args()
 
     import torch
@@ -57,26 +59,34 @@ def main():
     del big
     with open(a.out, "w") as out:
         for n in a.sizes:
-            A = torch.randn(n, n, device=dev)
-            B = torch.randn(n, n, device=dev)
-            C = torch.empty(n, n, device=dev)
+            for op in a.ops:
+                ta, tb = int(op[0] == "t"), int(op[1] == "t")
+                # storage: A is n x n either way; op(A) = A^T reads it transposed
+                A = torch.randn(n, n, device=dev)
+                B = torch.randn(n, n, device=dev)
+                C = torch.empty(n, n, device=dev)
+                opA = A.t() if ta else A
+                opB = B.t() if tb else B
 
-            def ours():
-                rc = fg.sgemm(n, n, n, 1.0, A, n, B, n, 0.0, C, n, stream.cuda_stream)
-                if rc:
-                    raise fg.Fp32GemmError(rc)
+                def ours():
+                    rc = fg.sgemm_ex(ta, tb, n, n, n, 1.0, A, n, B, n, 0.0, C, n, stream.cuda_stream)
+                    if rc:
+                        raise fg.Fp32GemmError(rc)
 
-            us_ours = timed(ours)
-            us_vendor = timed(lambda: torch.matmul(A, B))
-            ref = torch.matmul(A.double(), B.double())
-            err = float(((C.double() - ref).abs() / (A.abs().double() @ B.abs().double())).max())
-            rec = {"n": n, "us": round(us_ours, 3), "tflops": round(2 * n ** 3 / us_ours / 1e6, 3),
-                   "vendor_us": round(us_vendor, 3),
-                   "vendor_tflops": round(2 * n ** 3 / us_vendor / 1e6, 3),
-                   "ratio": round(us_vendor / us_ours, 3), "max_rel_err": err,
-                   "config": fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, n, n, n))}
-            print(json.dumps(rec), flush=True)
-            out.write(json.dumps(rec) + "\n")
+                us_ours = timed(ours)
+                us_vendor = timed(lambda: torch.matmul(opA, opB))
+                ref = torch.matmul(opA.double(), opB.double())
+                err = float(((C.double() - ref).abs() /
+                             (opA.abs().double() @ opB.abs().double())).max())
+                rec = {"n": n, "op": op, "us": round(us_ours, 3),
+                       "tflops": round(2 * n ** 3 / us_ours / 1e6, 3),
+                       "vendor_us": round(us_vendor, 3),
+                       "vendor_tflops": round(2 * n ** 3 / us_vendor / 1e6, 3),
+                       "ratio": round(us_vendor / us_ours, 3), "max_rel_err": err,
+                       "config": fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, n, n, n))}
+                print(json.dumps(rec), flush=True)
+                out.write(json.dumps(rec) + "\n")
+                del A, B, C
 
 
 if __name__ == "__main__":

@@ -33,9 +33,10 @@
  *  - Asynchrony: work is enqueued on `stream` (NULL = the null stream) and
  *    the call returns without synchronising.
  *  - Return value: 0 on success; -p when argument p (1-based, in the order of
- *    sgemm's parameter list) is invalid; FP32GEMM_ERR_CONFIG for an unknown
- *    configuration id; a positive hipError_t value when a HIP call or kernel
- *    launch fails.  Nothing is enqueued when a negative code is returned.
+ *    the routine's own parameter list) is invalid; FP32GEMM_ERR_CONFIG for an
+ *    unknown configuration id; a positive hipError_t value when a HIP call or
+ *    kernel launch fails.  Nothing is enqueued when a negative code is
+ *    returned.
  *  - Threads: every entry point is reentrant and keeps no per-call state;
  *    calls on different streams may run concurrently.  The library allocates
  *    no device memory.
@@ -75,6 +76,45 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
           fp32gemm_stream_t stream);
+
+/*
+ * Transposed operands.  op(X) = X for FP32GEMM_OP_N and X^T for FP32GEMM_OP_T.
+ * C[M x N] <- alpha * op(A)[M x K] . op(B)[K x N] + beta * C, row-major
+ * storage: A is M x K (lda >= K) for N, or stored K x M (lda >= M) with
+ * op(A)[i][k] = A[k * lda + i] for T; B is K x N (ldb >= N) for N, or stored
+ * N x K (ldb >= K) with op(B)[k][j] = B[j * ldb + k] for T.  These are the
+ * projection products of a transformer layer ("GPU GEMM 优化完全拆解（一）",
+ * section "LLM 推理本质上是 GEMM 的串联": QKV, Q K^T, FFN), where weights and
+ * keys are commonly stored transposed.  The 128-bit path needs 16-byte
+ * aligned operands whose contiguous dimension and leading dimension are
+ * multiples of 4.  With both operands as given and M <= 8 the call runs the
+ * GEMV kernel, as sgemm does.  Argument positions for error codes: transA 1,
+ * transB 2, M 3, N 4, K 5, alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12,
+ * ldc 13, stream 14.
+ */
+#define FP32GEMM_OP_N 0
+#define FP32GEMM_OP_T 1
+int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha,
+             const float *A, int lda, const float *B, int ldb, float beta,
+             float *C, int ldc, fp32gemm_stream_t stream);
+
+/*
+ * batch_count independent products of the same shape: entry b uses
+ * A + b * strideA, B + b * strideB and C + b * strideC (element strides).
+ * strideA or strideB may be 0 (one operand shared by every entry); the C
+ * entries must not overlap: strideC >= (M - 1) * ldc + N when
+ * batch_count > 1.  Per-head attention products (Q K^T and P V for every
+ * head) are this shape.  0 <= batch_count <= 65535; batch_count == 0 does
+ * nothing.  Argument positions: transA 1, transB 2, M 3, N 4, K 5, alpha 6,
+ * A 7, lda 8, strideA 9, B 10, ldb 11, strideB 12, beta 13, C 14, ldc 15,
+ * strideC 16, batch_count 17, stream 18.
+ */
+int sgemm_strided_batched(int transA, int transB, int M, int N, int K,
+                          float alpha, const float *A, int lda,
+                          long long strideA, const float *B, int ldb,
+                          long long strideB, float beta, float *C, int ldc,
+                          long long strideC, int batch_count,
+                          fp32gemm_stream_t stream);
 
 /* Human-readable text for a return code (static storage, never NULL). */
 const char *fp32gemm_strerror(int code);

@@ -82,6 +82,44 @@ def test_quick_returns_need_no_gpu(lib):
     assert call(fg.sgemm, K=0, lda=1, beta=1.0, A=None, B=None) == 0
 
 
+EX = dict(ta=0, tb=0, M=4, N=4, K=4, alpha=1.0, A=16, lda=4, B=16, ldb=4, beta=0.0, C=16, ldc=4)
+
+
+def call_ex(**kw):
+    a = dict(EX, **kw)
+    return fg.sgemm_ex(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+                       a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ta=2), -1), (dict(tb=-1), -2), (dict(M=-1), -3), (dict(N=-1), -4), (dict(K=-1), -5),
+    (dict(A=None), -7), (dict(K=8, lda=4), -8), (dict(ta=1, M=8, lda=4, ldc=4, N=4), -8),
+    (dict(B=None), -9), (dict(tb=1, K=8, lda=8, ldb=4), -10), (dict(C=None), -12),
+    (dict(N=8, ldb=8, ldc=4), -13),
+])
+def test_sgemm_ex_argument_checks(lib, kw, code):
+    assert call_ex(**kw) == code
+
+
+def test_batched_argument_checks(lib):
+    def b(**kw):
+        a = dict(ta=0, tb=0, M=4, N=4, K=4, alpha=1.0, A=16, lda=4, sA=16, B=16, ldb=4, sB=16,
+                 beta=0.0, C=16, ldc=4, sC=16, batch=2)
+        a.update(kw)
+        return fg.sgemm_strided_batched(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"],
+                                        a["A"], a["lda"], a["sA"], a["B"], a["ldb"], a["sB"],
+                                        a["beta"], a["C"], a["ldc"], a["sC"], a["batch"], 0)
+    assert b(sA=-1) == -9
+    assert b(sB=-4) == -12
+    assert b(sC=8) == -16          # C entries would overlap
+    assert b(batch=-1) == -17
+    assert b(batch=70000) == -17
+    assert b(batch=0, A=None, B=None, C=None) == 0   # nothing to do
+    assert b(M=0, C=None) == 0
+    assert b(alpha=0.0, beta=1.0, A=None, B=None) == 0
+    assert fg.strerror(-17) == "invalid argument 17"
+
+
 def test_gemv_batch_range(lib):
     assert call(fg.sgemv, M=9) == -1
     assert call(fg.sgemv, M=0) == -1
