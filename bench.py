@@ -201,7 +201,32 @@ def main():
             "warm_single_buffer": {"us_per_call": round(warm_us, 3),
                                    "GB/s": round(gbytes / (warm_us * 1e-6) / 1e9, 1)},
         }
+        # the same decode with the weight stored N x K (a linear layer's
+        # layout, y = x W^T): sgemm_ex(N, T) runs the row-dot kernel
+        dWt = [dWs[0].t().contiguous()]
         del dWs
+        for _ in range(nbuf - 1):
+            dWt.append(dWt[0].clone())
+
+        def tstep(i):
+            check(fg.sgemm_ex(0, 1, gw.M, gw.N, gw.K, gw.alpha, dX, gw.K, dWt[i % nbuf], gw.K,
+                              gw.beta, dY, gw.N, sp))
+
+        for i in range(32):
+            tstep(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.gemv_steps):
+            tstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tus = e0.elapsed_time(e1) / args.gemv_steps * 1e3
+        tbps = gbytes / (tus * 1e-6) / 1e9
+        gemv["weight_stored_transposed"] = {
+            "call": "sgemm_ex(transA=0, transB=1)", "us_per_call": round(tus, 3),
+            "GB/s": round(tbps, 1), "frac": round(tbps / acc.PEAK_HBM_GBPS, 4),
+            "traffic": stored_traffic("gemv_nt_m1_4096", GEMV_SOURCES)}
+        del dWt
 
     # ---------------- CPU oracle on a bounded sample ----------------
     cpu = None

@@ -71,12 +71,12 @@ int run_gemm(int cfg, int ta, int tb, const GemmArgs &a, hipStream_t s) {
   return (int)c.launch[2 * ta + tb](a, vec4_ok(a, ta, tb), kGroups[cfg % kNumGroups], s);
 }
 
-int run_gemv(int cfg, const GemmArgs &a, hipStream_t s) {
+int run_gemv(int cfg, int ta, const GemmArgs &a, hipStream_t s) {
   int n = 0;
   const GemvConfig *cfgs = gemv_configs(&n);
   if (cfg < 0) cfg = select_gemv_config(a.M, a.N, a.K);
   if (cfg >= n) return FP32GEMM_ERR_CONFIG;
-  return (int)cfgs[cfg].launch(a, s);
+  return (int)cfgs[cfg].launch(a, ta, s);
 }
 
 GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -103,7 +103,7 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (M <= 8) return run_gemv(-1, a, s);
+  if (M <= 8) return run_gemv(-1, 0, a, s);
   return run_gemm(-1, 0, 0, a, s);
 }
 
@@ -115,7 +115,7 @@ int sgemv(int M, int N, int K, float alpha, const float *A, int lda, const float
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  return run_gemv(-1, a, s);
+  return run_gemv(-1, 0, a, s);
 }
 
 int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
@@ -125,7 +125,8 @@ int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const flo
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (M <= 8 && !transA && !transB) return run_gemv(-1, a, s);
+  if (gemv_supported(a, transA))
+    return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
   return run_gemm(-1, transA, transB, a, s);
 }
 
@@ -209,7 +210,7 @@ int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha, const 
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  return run_gemv(cfg, a, s);
+  return run_gemv(cfg, 0, a, s);
 }
 
 }  // extern "C"

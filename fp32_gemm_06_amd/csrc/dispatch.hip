@@ -113,8 +113,16 @@ int select_gemv_config(int M, int N, int K) {
       const int id = find_gemv(e.name);
       if (id >= 0) return id;
     }
-  // Narrow column blocks keep enough workgroups in flight unless N is huge.
-  const int id = find_gemv(N >= 65536 ? "c64_w16_u8" : "c16_w8_u8");
+  // Wider column stripes read longer runs of each row of W (64, 128 or 256
+  // bytes), which the memory system serves faster, but give fewer
+  // workgroups.  The sweep over N from 1024 to 65536 is fastest with the
+  // widest stripe that still leaves about 160 workgroups or more.
+  (void)K;
+  const char *name = N >= 160 * 64   ? "c64_w8_u4"
+                     : N >= 256 * 32 ? "c32_w8_u4"
+                     : M >= 4        ? "c16_w4_u8"
+                                     : "c16_w8_u4";
+  const int id = find_gemv(name);
   return id >= 0 ? id : 0;
 }
 

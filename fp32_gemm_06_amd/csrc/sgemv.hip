@@ -21,8 +21,12 @@
 //    per XCD concentrates its traffic on few memory channels;
 //  * lanes are grouped LPR to a row (one float4 each); a wave instruction
 //    reads RPI = 64 / LPR rows; lane group g of wave w takes U consecutive
-//    rows per pass, so its X values are U consecutive floats per batch row;
-//  * every lane keeps U loads of W in flight and M x 4 fp32 accumulators;
+//    rows per pass of ROWS = NW * RPI * U rows;
+//  * passes run two deep: the W values and the X chunk of pass p + 1 are in
+//    flight while pass p is multiplied (W in two register sets, X through a
+//    double buffer in LDS, read back as float4 over a lane group's U rows).
+//    The loop body has no branches: rows past K read zeros through an
+//    out-of-range buffer offset, so passes run in whole pairs;
 //  * partial sums are added across the lane groups of a wave with a fixed
 //    butterfly, then across waves in LDS in wave order: the summation order
 //    does not depend on timing, so results are bit-reproducible.
@@ -31,15 +35,23 @@
 namespace fp32gemm {
 namespace {
 
-template <int MR, bool VEC, bool XVEC, int CBW, int NW, int U>
+// Largest lda for op(A) = A^T that keeps a pass's X offsets within 31 bits
+// (both GEMV kernels stage at most 2048 values of K at a time).
+constexpr int kGemvMaxLdaT = 1 << 17;
+
+template <int MR, bool VEC, int CBW, int NW, int U>
 __global__ void __launch_bounds__(NW * 64)
-sgemv_kernel(GemmArgs a) {
+sgemv_kernel(GemmArgs a, int transA) {
   constexpr int VW = VEC ? 4 : 1;     // columns per lane
   constexpr int LPR = CBW / VW;       // lanes per row
   constexpr int RPI = 64 / LPR;       // rows per wave instruction
-  constexpr int ROWS = NW * RPI * U;  // rows per workgroup pass
+  constexpr int ROWS = NW * RPI * U;  // rows of W per pass
+  constexpr int THREADS = NW * 64;
+  constexpr int XN = MR * ROWS;                        // X values per pass
+  constexpr int XPT = (XN + THREADS - 1) / THREADS;    // staged per thread
   static_assert(64 % LPR == 0 && CBW % VW == 0, "lane mapping");
-  static_assert(!XVEC || U % 4 == 0, "X is read in float4 pieces");
+  static_assert(U % 4 == 0, "X is read back in float4 pieces");
+  __shared__ __attribute__((aligned(16))) float xs[2][MR][ROWS];
   __shared__ float red[NW][MR][CBW];
 
   const int tid = threadIdx.x;
@@ -57,27 +69,20 @@ sgemv_kernel(GemmArgs a) {
                      : bid;
   const int n0 = cb * CBW;
   const bool col_ok = n0 + cl < a.N;  // VEC: N % 4 == 0, so the float4 is whole
+  const int K = a.K;
+  const int wrow = wave * RPI * U;    // first row of this wave in a pass
+  const int rl = wrow + g * U;        // first row of this lane in a pass
+  // X element (m, k) sits at A + k * xk + m * xm
+  const uint32_t xk = transA ? (uint32_t)a.lda : 1u, xm = transA ? 1u : (uint32_t)a.lda;
 
-  float acc[MR][VW];
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int e = 0; e < VW; ++e) acc[m][e] = 0.0f;
-
-  const int ldb = a.ldb, lda = a.lda;
-  for (int k0 = 0; k0 < a.K; k0 += ROWS) {
-    // this lane's rows: k0 + wave * RPI * U + g * U + u, u < U.  The wave's
-    // first row goes into the buffer base so byte offsets stay below 2^31.
-    const int kw = k0 + wave * RPI * U;
-    const int r0 = g * U;
-    const int nrows = a.K - kw - r0;  // rows of this lane still inside K
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)kw * ldb + n0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + kw);
-    float w[U][VW];
+  // W rows k0 + rl + u of this lane's columns; the wave's first row goes
+  // into the buffer base so byte offsets stay small
+  auto load_w = [&](float (&w)[U][VW], int k0) {
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)(k0 + wrow) * a.ldb + n0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = col_ok && u < nrows;
-      const uint32_t off = ok ? (uint32_t)((r0 + u) * ldb + cl) * 4u : kOob;
+      const bool ok = col_ok && k0 + rl + u < K;
+      const uint32_t off = ok ? (uint32_t)((g * U + u) * a.ldb + cl) * 4u : kOob;
       if constexpr (VEC) {
         const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
 #pragma unroll
@@ -86,31 +91,66 @@ sgemv_kernel(GemmArgs a) {
         w[u][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0));
       }
     }
+  };
+  // X of the pass at k0: value i = m * ROWS + kk for i = tid + j * THREADS
+  // (consecutive threads read consecutive k of one row of op(A))
+  auto load_x = [&](float (&x)[XPT], int k0) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + (size_t)k0 * xk);
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float x[U];
-      if constexpr (XVEC) {
-        // rows kw + r0 + u start on a multiple of 4 and K % 4 == 0, so each
-        // float4 of X is entirely inside or entirely outside K
-#pragma unroll
-        for (int q = 0; q < U / 4; ++q) {
-          const uint32_t off = 4 * q < nrows ? (uint32_t)(m * lda + r0 + 4 * q) * 4u : kOob;
-          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t off = u < nrows ? (uint32_t)(m * lda + r0 + u) * 4u : kOob;
-          x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < VW; ++e) acc[m][e] += x[u] * w[u][e];
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + j * THREADS, m = i / ROWS, kk = i % ROWS;
+      const bool ok = i < XN && k0 + kk < K;
+      const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
+      x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     }
+  };
+  auto store_x = [&](const float (&x)[XPT], int buf) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + j * THREADS;
+      if (XN % THREADS == 0 || i < XN) (&xs[buf][0][0])[i] = x[j];
+    }
+  };
+
+  float acc[MR][VW];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[m][e] = 0.0f;
+  auto multiply = [&](const float (&w)[U][VW], int buf) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int q = 0; q < U / 4; ++q) {
+        const floatx4 xv = *reinterpret_cast<const floatx4 *>(&xs[buf][m][rl + 4 * q]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[m][e] += xv[t] * w[4 * q + t][e];
+      }
+  };
+
+  float wa[U][VW], wb[U][VW];
+  float xr[XPT];
+  load_x(xr, 0);
+  load_w(wa, 0);
+  store_x(xr, 0);
+  __syncthreads();
+  // the scheduling barriers keep each prefetch ahead of the multiply that
+  // waits on the previous pass
+  for (int k0 = 0; k0 < K; k0 += 2 * ROWS) {
+    load_x(xr, k0 + ROWS);
+    load_w(wb, k0 + ROWS);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(wa, 0);
+    store_x(xr, 1);
+    __syncthreads();
+    load_x(xr, k0 + 2 * ROWS);
+    load_w(wa, k0 + 2 * ROWS);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(wb, 1);
+    store_x(xr, 0);
+    __syncthreads();
   }
 
   // Butterfly over the row groups of the wave (lane bits above the column bits).
@@ -143,6 +183,197 @@ sgemv_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M product with the weight stored transposed: op(B) = B^T, B stored
+// N x K (the usual layout of a linear layer's weight, y = x W^T).  Output
+// (m, n) is the dot product of row m of op(A) with row n of the stored B, a
+// contiguous run of K floats, so the weight streams with 1 KB wave
+// instructions (64 lanes x 16 bytes) and none of the column-stripe pattern of
+// the other layout.  Each wave owns RW consecutive rows of B and walks K in
+// chunks of CH floats, two chunks deep: the weights and the X values of chunk
+// c + 1 are in flight while chunk c is multiplied (X through a double buffer
+// in LDS, weights in two register sets).  The loop body has no branches:
+// loads past K (or past N) take an out-of-range buffer offset and read zeros,
+// so a pair of chunks always runs whole and the over-fetch adds exact zeros.
+// Partial dot products stay in registers and are added across the wave with
+// a fixed butterfly, so the result does not depend on timing.
+// ---------------------------------------------------------------------------
+constexpr int kRowsWaves = 4;
+constexpr int kRowsThreads = kRowsWaves * 64;
+
+template <int MR, bool VEC, int RW>
+__global__ void __launch_bounds__(kRowsThreads)
+sgemv_rows_kernel(GemmArgs a, int transA) {
+  constexpr int CH = MR <= 4 ? 1024 : 512;   // K floats per chunk
+  constexpr int VW = VEC ? 4 : 1;            // weight floats per lane per position
+  constexpr int STEP = 64 * VW;              // k covered by one wave instruction
+  constexpr int POS = CH / STEP;             // positions per chunk
+  constexpr int XPT = MR * CH / kRowsThreads;  // X floats staged per thread per chunk
+  __shared__ __attribute__((aligned(16))) float xs[2][MR * CH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = (blockIdx.x * kRowsWaves + wave) * RW;  // first row of this wave
+  const int K = a.K;
+  // X element (m, k0 + kk) sits at A + k0 * xk + kk * xk + m * xm
+  const uint32_t xk = transA ? (uint32_t)a.lda : 1u, xm = transA ? 1u : (uint32_t)a.lda;
+
+  __amdgpu_buffer_rsrc_t rs[RW];
+  bool live[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    live[r] = n0 + r < a.N;
+    rs[r] = make_rsrc(a.B + (live[r] ? (size_t)(n0 + r) * a.ldb : 0));
+  }
+
+  // weights of the chunk at k0: RW rows x POS positions, zeros past K or N
+  auto load_w = [&](float (&w)[RW][POS][VW], int k0) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int p = 0; p < POS; ++p) {
+        const int k = k0 + p * STEP + lane * VW;
+        const uint32_t off = live[r] && k < K ? (uint32_t)k * 4u : kOob;
+        if constexpr (VEC) {
+          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs[r], off, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[r][p][e] = v[e];
+        } else {
+          w[r][p][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs[r], off, 0, 0));
+        }
+      }
+  };
+  // X of the chunk at k0, element i = m * CH + kk for i = tid + j * threads
+  // (consecutive lanes read consecutive k), zeros past K
+  auto load_x = [&](float (&x)[XPT], int k0) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + (size_t)k0 * xk);
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + j * kRowsThreads, m = i / CH, kk = i % CH;
+      const uint32_t off = k0 + kk < K ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
+      x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+    }
+  };
+  auto store_x = [&](const float (&x)[XPT], int buf) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xs[buf][tid + j * kRowsThreads] = x[j];
+  };
+
+  float acc[MR][RW];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[m][r] = 0.0f;
+  auto multiply = [&](const float (&w)[RW][POS][VW], int buf) {
+#pragma unroll
+    for (int p = 0; p < POS; ++p) {
+      const int k = p * STEP + lane * VW;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float x[VW];
+        if constexpr (VEC) {
+          const floatx4 v = *reinterpret_cast<const floatx4 *>(&xs[buf][m * CH + k]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = v[e];
+        } else {
+          x[0] = xs[buf][m * CH + k];
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[m][r] += x[e] * w[r][p][e];
+      }
+    }
+  };
+
+  const int nc = (K + CH - 1) / CH;
+  float wa[RW][POS][VW], wb[RW][POS][VW];
+  float xr[XPT];
+  load_x(xr, 0);
+  load_w(wa, 0);
+  store_x(xr, 0);
+  __syncthreads();
+  // the scheduling barriers keep each prefetch ahead of the multiply that
+  // waits on the previous chunk (left alone, the scheduler interleaves them
+  // and the waits then cover the prefetch too)
+  for (int c = 0; c < nc; c += 2) {
+    load_x(xr, (c + 1) * CH);
+    load_w(wb, (c + 1) * CH);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(wa, 0);
+    store_x(xr, 1);
+    __syncthreads();
+    load_x(xr, (c + 2) * CH);
+    load_w(wa, (c + 2) * CH);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(wb, 1);
+    store_x(xr, 0);
+    __syncthreads();
+  }
+
+  // butterfly over the 64 lanes; lane m * RW + r then writes output (m, n0 + r)
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[m][r] += __shfl_xor(acc[m][r], s, 64);
+  float sum = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      if (lane == m * RW + r) sum = acc[m][r];
+  const int m = lane / RW, n = n0 + lane % RW;
+  if (lane < MR * RW && n < a.N) {
+    float *y = a.C + (size_t)m * a.ldc + n;
+    float out = a.alpha * sum;
+    if (a.beta != 0.0f) out += a.beta * *y;
+    *y = out;
+  }
+}
+
+template <bool VEC, int RW>
+hipError_t launch_rows_rw(const GemmArgs &a, int transA, hipStream_t s) {
+  const long long wgs = ((long long)a.N + kRowsWaves * RW - 1) / (kRowsWaves * RW);
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)wgs), block(kRowsThreads);
+  switch (a.M) {
+#define FP32GEMM_ROWS_CASE(MR) \
+  case MR: hipLaunchKernelGGL((sgemv_rows_kernel<MR, VEC, RW>), grid, block, 0, s, a, transA); break;
+    FP32GEMM_ROWS_CASE(1)
+    FP32GEMM_ROWS_CASE(2)
+    FP32GEMM_ROWS_CASE(3)
+    FP32GEMM_ROWS_CASE(4)
+    FP32GEMM_ROWS_CASE(5)
+    FP32GEMM_ROWS_CASE(6)
+    FP32GEMM_ROWS_CASE(7)
+    FP32GEMM_ROWS_CASE(8)
+#undef FP32GEMM_ROWS_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemv_supported(const GemmArgs &a, int transA) {
+  return a.M >= 1 && a.M <= 8 && (!transA || a.lda <= kGemvMaxLdaT);
+}
+
+// Rows per wave: one for M <= 3 (the most waves, which keeps the most loads
+// in flight), two from M = 4 on (each staged X value then feeds two rows).
+// A timing sweep over decode shapes (N, K in 1024 .. 32000) picked these.
+hipError_t launch_gemv_rows(const GemmArgs &a, int transA, int rows_per_wave, hipStream_t s) {
+  if (!gemv_supported(a, transA)) return hipErrorInvalidValue;
+  const bool vec = ((uintptr_t)a.B % 16 == 0) && a.K % 4 == 0 && a.ldb % 4 == 0;
+  const int rw = rows_per_wave > 0 ? rows_per_wave : a.M >= 4 ? 2 : 1;
+  if (vec) return rw >= 2 ? launch_rows_rw<true, 2>(a, transA, s) : launch_rows_rw<true, 1>(a, transA, s);
+  return rw >= 2 ? launch_rows_rw<false, 2>(a, transA, s) : launch_rows_rw<false, 1>(a, transA, s);
+}
+
+namespace {
+
 // C <- beta * C for every batch entry (blockIdx.z); beta == 0 stores zeros
 // without reading C.
 __global__ void __launch_bounds__(256)
@@ -156,15 +387,15 @@ scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta) {
   }
 }
 
-template <bool VEC, bool XVEC, int CBW, int NW, int U>
-hipError_t launch_cfg(const GemmArgs &a, hipStream_t s) {
+template <bool VEC, int CBW, int NW, int U>
+hipError_t launch_cfg(const GemmArgs &a, int transA, hipStream_t s) {
   const long long blocks = ((long long)a.N + CBW - 1) / CBW;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(NW * 64);
   switch (a.M) {
-#define FP32GEMM_GEMV_CASE(MR)                                                                  \
-  case MR:                                                                                      \
-    hipLaunchKernelGGL((sgemv_kernel<MR, VEC, XVEC, CBW, NW, U>), grid, block, 0, s, a); break;
+#define FP32GEMM_GEMV_CASE(MR)                                                                   \
+  case MR:                                                                                       \
+    hipLaunchKernelGGL((sgemv_kernel<MR, VEC, CBW, NW, U>), grid, block, 0, s, a, transA); break;
     FP32GEMM_GEMV_CASE(1)
     FP32GEMM_GEMV_CASE(2)
     FP32GEMM_GEMV_CASE(3)
@@ -179,15 +410,12 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 128-bit loads of W need B 16-byte aligned and N, ldb multiples of 4; of X,
-// A 16-byte aligned and K, lda multiples of 4.
+// 128-bit loads of W need B 16-byte aligned and N, ldb multiples of 4.
 template <int CBW, int NW, int U>
-hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemv(const GemmArgs &a, int transA, hipStream_t s) {
+  if (!gemv_supported(a, transA)) return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
-  const bool xvec = ((uintptr_t)a.A % 16 == 0) && a.K % 4 == 0 && a.lda % 4 == 0;
-  if (vec)
-    return xvec ? launch_cfg<true, true, CBW, NW, U>(a, s) : launch_cfg<true, false, CBW, NW, U>(a, s);
-  return xvec ? launch_cfg<false, true, CBW, NW, U>(a, s) : launch_cfg<false, false, CBW, NW, U>(a, s);
+  return vec ? launch_cfg<true, CBW, NW, U>(a, transA, s) : launch_cfg<false, CBW, NW, U>(a, transA, s);
 }
 
 }  // namespace
@@ -198,10 +426,10 @@ const GemvConfig *gemv_configs(int *count) {
       {"c16_w8_u4", 16, 8, 4, &launch_gemv<16, 8, 4>},
       {"c16_w16_u4", 16, 16, 4, &launch_gemv<16, 16, 4>},
       {"c16_w4_u8", 16, 4, 8, &launch_gemv<16, 4, 8>},
-      {"c16_w8_u16", 16, 8, 16, &launch_gemv<16, 8, 16>},
-      {"c16_w16_u8", 16, 16, 8, &launch_gemv<16, 16, 8>},
+      {"c16_w4_u16", 16, 4, 16, &launch_gemv<16, 4, 16>},
+      {"c32_w8_u4", 32, 8, 4, &launch_gemv<32, 8, 4>},
       {"c32_w8_u8", 32, 8, 8, &launch_gemv<32, 8, 8>},
-      {"c64_w16_u8", 64, 16, 8, &launch_gemv<64, 16, 8>},
+      {"c64_w8_u4", 64, 8, 4, &launch_gemv<64, 8, 4>},
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -4,7 +4,7 @@
 
 <run dir> holds the CSV output of one kernel-trace run (trace/) and of
 counter runs (pmc*/), each made with ``--output-format csv``.  Writes
-<out prefix>_<kernel>.md summaries and, for the SGEMM and GEMV kernels,
+<out prefix>_<kernel>.md summaries and, for the SGEMM and the two GEMV kernels,
 <out prefix>_<kernel>_traffic.json with HBM bytes per launch.
 
 HBM bytes come from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
@@ -27,6 +27,7 @@ CSRC = os.path.join(ROOT, "fp32_gemm_06_amd", "csrc")
 KERNELS = {
     "sgemm_4092": ("sgemm_kernel", ["sgemm_kernel.h", "sgemm_nn.hip", "common.h", "tune_table.inc"]),
     "gemv_m1_4096": ("sgemv_kernel<1,", ["sgemv.hip", "common.h", "tune_table.inc"]),
+    "gemv_nt_m1_4096": ("sgemv_rows_kernel<1,", ["sgemv.hip", "common.h", "tune_table.inc"]),
 }
 CALIB = "neg_kernel"
 CALIB_BYTES = 256 << 20

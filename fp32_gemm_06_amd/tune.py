@@ -48,6 +48,16 @@ SHAPES = [
     ("gemv", 1, 4096, 4096, 1.0, 0.0),
     ("gemv", 4, 4096, 4096, 1.0, 0.0),
     ("gemv", 8, 4096, 4096, 1.0, 0.0),
+    ("gemv", 1, 1024, 1024, 1.0, 0.0),
+    ("gemv", 1, 2048, 2048, 1.0, 0.0),
+    ("gemv", 1, 8192, 8192, 1.0, 0.0),
+    ("gemv", 1, 11008, 4096, 1.0, 0.0),
+    ("gemv", 8, 11008, 4096, 1.0, 0.0),
+    ("gemv", 1, 4096, 11008, 1.0, 0.0),
+    ("gemv", 8, 4096, 11008, 1.0, 0.0),
+    ("gemv", 1, 16384, 4096, 1.0, 0.0),
+    ("gemv", 1, 32000, 4096, 1.0, 0.0),
+    ("gemv", 1, 65536, 1024, 1.0, 0.0),
 ]
 
 

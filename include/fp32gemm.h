@@ -87,8 +87,12 @@ int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
  * section "LLM 推理本质上是 GEMM 的串联": QKV, Q K^T, FFN), where weights and
  * keys are commonly stored transposed.  The 128-bit path needs 16-byte
  * aligned operands whose contiguous dimension and leading dimension are
- * multiples of 4.  With both operands as given and M <= 8 the call runs the
- * GEMV kernel, as sgemm does.  Argument positions for error codes: transA 1,
+ * multiples of 4.  M <= 8 runs a GEMV kernel: with op(B) = B the one sgemm
+ * uses; with op(B) = B^T (a linear layer's weight stored N x K, y = x W^T) a
+ * row-dot kernel that streams each stored row of B contiguously.  Either
+ * takes op(A) = A^T as well, up to lda = 2^17 (beyond that the tiled kernel
+ * runs).  Both reduce in a fixed order, so results are bit-reproducible.
+ * Argument positions for error codes: transA 1,
  * transB 2, M 3, N 4, K 5, alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12,
  * ldc 13, stream 14.
  */

@@ -48,3 +48,27 @@ def test_decode_sizes_normal():
         got, _ = run_hip(X, W, Y0, 1.0, 0.0)
         assert_parity(got, oracle.sgemm(X, W, Y0, 1.0, 0.0), oracle.bound(X, W, Y0, 1.0, 0.0),
                       f"decode M={M}")
+
+
+@pytest.mark.parametrize("M", range(1, 9))
+def test_transposed_x(M):
+    """op(A) = A^T (A stored K x M) through sgemm_ex: the same kernel reads X
+    with strides swapped.  K = 5000 spans an odd number of passes."""
+    from test_transpose_batched import _case, run_batched
+    N, K = 530, 5000
+    As, Bs, Cs = _case(7000 + M, M, N, K)
+    (got,), ok = run_batched(1, 0, As, Bs, Cs, 1.0, 0.5, pads=(5, 4, 3), offset=1)
+    assert ok, "write outside C"
+    assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"M={M} op(A)=A^T")
+
+
+@pytest.mark.parametrize("tb", (0, 1))
+def test_transposed_x_huge_lda_falls_back(tb):
+    """lda beyond the GEMV kernels' X-offset range sends op(A) = A^T to the
+    tiled kernel, which gives the same exact result."""
+    from test_transpose_batched import _case, run_batched
+    M, N, K = 2, 50, 3
+    As, Bs, Cs = _case(7100 + tb, M, N, K)
+    (got,), ok = run_batched(1, tb, As, Bs, Cs, 1.0, 0.5, pads=(140000 - M, 0, 0))
+    assert ok
+    assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"huge lda tb={tb}")
