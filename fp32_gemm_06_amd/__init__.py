@@ -37,8 +37,12 @@ _BATCHED_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, cty
                      ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
                      ctypes.c_void_p]
 
+_SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+
 # Every symbol include/fp32gemm.h declares.
-EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "fp32gemm_strerror",
+EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_splitk",
+           "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits", "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
            "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
 
@@ -64,6 +68,12 @@ def lib():
         L.sgemm_ex.restype = ctypes.c_int
         L.sgemm_strided_batched.argtypes = _BATCHED_ARGTYPES
         L.sgemm_strided_batched.restype = ctypes.c_int
+        L.sgemm_splitk.argtypes = _SPLITK_ARGTYPES
+        L.sgemm_splitk.restype = ctypes.c_int
+        L.sgemm_splitk_workspace_size.argtypes = [ctypes.c_int] * 4
+        L.sgemm_splitk_workspace_size.restype = ctypes.c_size_t
+        L.fp32gemm_splitk_splits.argtypes = [ctypes.c_int] * 3
+        L.fp32gemm_splitk_splits.restype = ctypes.c_int
         L.fp32gemm_strerror.argtypes = [ctypes.c_int]
         L.fp32gemm_strerror.restype = ctypes.c_char_p
         L.fp32gemm_num_configs.argtypes = [ctypes.c_int]
@@ -122,6 +132,25 @@ def sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ld
     return lib().sgemm_strided_batched(transA, transB, M, N, K, alpha, _addr(A), lda, strideA,
                                        _addr(B), ldb, strideB, beta, _addr(C), ldc, strideC,
                                        batch_count, _stream(stream))
+
+
+def sgemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                 workspace, workspace_bytes, stream=None) -> int:
+    """sgemm_ex computed as K chunks plus a fixed-order reduction; the caller
+    provides the workspace (sgemm_splitk_workspace_size bytes)."""
+    return lib().sgemm_splitk(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                              _addr(C), ldc, splits, _addr(workspace), workspace_bytes,
+                              _stream(stream))
+
+
+def sgemm_splitk_workspace_size(M, N, K, splits=0) -> int:
+    """Workspace bytes sgemm_splitk needs (0 when it runs as one chunk)."""
+    return lib().sgemm_splitk_workspace_size(M, N, K, splits)
+
+
+def fp32gemm_splitk_splits(M, N, K) -> int:
+    """The number of K chunks sgemm_splitk uses when splits = 0."""
+    return lib().fp32gemm_splitk_splits(M, N, K)
 
 
 def fp32gemm_sgemm_with_config(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

@@ -13,6 +13,8 @@ namespace {
 // Largest leading dimension accepted: keeps every in-tile byte offset the
 // kernels form (at most 256 rows x ld x 4 bytes) inside 32 bits.
 constexpr int kMaxLd = 1 << 20;
+// Most K chunks of a split-K call (one grid dimension).
+constexpr int kMaxSplits = 65535;
 
 int imax(int a, int b) { return a > b ? a : b; }
 
@@ -88,6 +90,7 @@ GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const f
   a.lda = lda; a.ldb = ldb; a.ldc = ldc;
   a.sA = a.sB = a.sC = 0;
   a.batch = 1;
+  a.k_total = 0;
   return a;
 }
 
@@ -145,6 +148,55 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alp
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
   return run_gemm(-1, transA, transB, a, s);
+}
+
+size_t sgemm_splitk_workspace_size(int M, int N, int K, int splits) {
+  if (M <= 8 || N <= 0 || K <= 0 || splits < 0 || splits > kMaxSplits) return 0;
+  int kc = 0;
+  const int chunks = splitk_chunk(K, splits > 0 ? splits : splitk_pick(M, N, K), &kc);
+  return chunks > 1 ? (size_t)chunks * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+int fp32gemm_splitk_splits(int M, int N, int K) {
+  if (M <= 8 || N <= 0 || K <= 0) return 1;
+  int kc = 0;
+  return splitk_chunk(K, splitk_pick(M, N, K), &kc);
+}
+
+int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
+                 const float *B, int ldb, float beta, float *C, int ldc, int splits, float *workspace,
+                 size_t workspace_bytes, fp32gemm_stream_t stream) {
+  GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemmEx, transA, transB, a);
+  if (rc) return rc;
+  if (splits < 0 || splits > kMaxSplits) return -14;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quick_return(a, s, &rc)) return rc;
+  int kc = 0;
+  const int chunks = M <= 8 ? 1 : splitk_chunk(K, splits > 0 ? splits : splitk_pick(M, N, K), &kc);
+  if (chunks <= 1) {  // one chunk: the plain routine (no workspace needed)
+    if (gemv_supported(a, transA))
+      return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
+    return run_gemm(-1, transA, transB, a, s);
+  }
+  if (workspace == nullptr) return -15;
+  if (workspace_bytes < (size_t)chunks * (size_t)M * (size_t)N * sizeof(float)) return -16;
+  // phase 1: chunk c of K as batch entry c, raw sums into workspace plane c
+  GemmArgs p = a;
+  p.K = kc;
+  p.k_total = K;
+  p.alpha = 1.0f;
+  p.beta = 0.0f;
+  p.C = workspace;
+  p.ldc = N;
+  p.sA = transA ? (long long)kc * lda : (long long)kc;
+  p.sB = transB ? (long long)kc : (long long)kc * ldb;
+  p.sC = (long long)M * N;
+  p.batch = chunks;
+  rc = run_gemm(model_gemm_config(M, N, chunks, nullptr), transA, transB, p, s);
+  if (rc) return rc;
+  // phase 2: C <- alpha * (sum of the planes, in order) + beta * C
+  return (int)launch_splitk_reduce(workspace, chunks, M, N, alpha, beta, C, ldc, s);
 }
 
 const char *fp32gemm_strerror(int code) {

@@ -19,6 +19,10 @@ struct GemmArgs {
   int lda, ldb, ldc;
   long long sA, sB, sC;  // element strides between batch entries
   int batch;             // number of products (1 for a single GEMM)
+  // Split-K: when > 0, entry b of the batch reduces over k in
+  // [b * K, min((b + 1) * K, k_total)) of the whole product (its operands are
+  // already offset by sA, sB); 0 for ordinary calls.
+  int k_total;
 };
 
 // Buffer-resource word 3 for gfx9-family raw buffers: 32-bit data format,
@@ -55,7 +59,7 @@ inline bool vec4_ok(const GemmArgs &a, bool ta, bool tb) {
                    a.sA % 4 == 0;
   const bool okB = ((uintptr_t)a.B % 16 == 0) && a.ldb % 4 == 0 && (tb ? a.K : a.N) % 4 == 0 &&
                    a.sB % 4 == 0;
-  return okA && okB;
+  return okA && okB && a.k_total % 4 == 0;
 }
 
 // ---- SGEMM (fp32 MFMA) family ---------------------------------------------
@@ -93,6 +97,15 @@ hipError_t launch_gemv_rows(const GemmArgs &a, int transA, int rows_per_wave, hi
 // C <- beta * C (beta == 0 writes zeros without reading C).
 hipError_t launch_scale(const GemmArgs &a, hipStream_t s);
 
+// Split-K (csrc/splitk.hip).  The K range is cut into chunks of kc floats (a
+// multiple of 32); splitk_chunk returns kc for `splits` requested chunks and
+// the number of chunks that leaves.  C <- alpha * sum_s ws[s] + beta * C,
+// summed in ascending s, where ws holds `splits` packed M x N partials.
+int splitk_chunk(int K, int splits, int *kc);
+int splitk_pick(int M, int N, int K);
+hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, float alpha, float beta,
+                                float *C, int ldc, hipStream_t s);
+
 // SGEMM configuration ids combine a tile shape with the tile-ordering group
 // (tile-rows per strip): id = tile_index * kNumGroups + group_index.
 constexpr int kNumGroups = 4;
@@ -103,6 +116,9 @@ const char *gemm_config_name(int id);
 
 // Per-shape table (generated by the tuning sweep) and size-class fallbacks.
 int select_gemm_config(int M, int N, int K);
+// The fallback model alone, for a grid of `mult` products of M x N (split-K
+// chunks); *rate receives the modelled TFLOP/s.
+int model_gemm_config(int M, int N, int mult, double *rate);
 int select_gemv_config(int M, int N, int K);
 
 }  // namespace fp32gemm

@@ -73,12 +73,7 @@ const char *gemm_config_name(int id) {
 // for fewer than four workgroups per CU.  Checked against the sweep, the
 // estimate picks the measured best tile at 1536^3, 2048^3, 3072^3, 512x4096
 // and 512x11008, and is within about 10% of the measured rate elsewhere.
-int select_gemm_config(int M, int N, int K) {
-  for (const ShapeEntry &e : kGemmTable)
-    if (e.M == M && e.N == N && e.K == K) {
-      const int id = find_gemm(e.name);
-      if (id >= 0) return id;
-    }
+int model_gemm_config(int M, int N, int mult, double *rate_out) {
   struct Candidate {
     const char *name;
     int bm, bn;
@@ -93,7 +88,7 @@ int select_gemm_config(int M, int N, int K) {
   int best = -1;
   double best_rate = -1.0;
   for (const Candidate &c : cands) {
-    const double tiles = (double)((M + c.bm - 1) / c.bm) * (double)((N + c.bn - 1) / c.bn);
+    const double tiles = (double)((M + c.bm - 1) / c.bm) * (double)((N + c.bn - 1) / c.bn) * mult;
     const double rounds = (double)(long long)((tiles + 255.0) / 256.0);
     double rate = c.full_rate * tiles / (rounds * 256.0);
     if (c.small && tiles < 1024.0) rate *= pow(tiles / 1024.0, 0.3);
@@ -103,8 +98,26 @@ int select_gemm_config(int M, int N, int K) {
       best = id;
     }
   }
-  (void)K;
+  if (rate_out) *rate_out = best_rate;
   return best >= 0 ? best : 0;
+}
+
+// Fallback for shapes the table does not list.  The pages observe that a grid
+// with too few blocks leaves the GPU idle ("CUDA 矩阵乘法优化", section
+// "10. cuBLAS 领先的性能差异").  The estimate per tile shape is its full-load
+// rate on MI355X (measured by the sweep) times its wave-quantization
+// efficiency over the 256 CUs (tiles / (rounds * 256), one 8-wave workgroup
+// per CU reaching full rate), and for the 4-wave 64x64 tile a further factor
+// for fewer than four workgroups per CU.  Checked against the sweep, the
+// estimate picks the measured best tile at 1536^3, 2048^3, 3072^3, 512x4096
+// and 512x11008, and is within about 10% of the measured rate elsewhere.
+int select_gemm_config(int M, int N, int K) {
+  for (const ShapeEntry &e : kGemmTable)
+    if (e.M == M && e.N == N && e.K == K) {
+      const int id = find_gemm(e.name);
+      if (id >= 0) return id;
+    }
+  return model_gemm_config(M, N, 1, nullptr);
 }
 
 int select_gemv_config(int M, int N, int K) {

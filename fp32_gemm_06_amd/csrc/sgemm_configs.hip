@@ -1,5 +1,6 @@
 // The SGEMM configuration table: tile shapes from FP32GEMM_TILES with the
 // launchers of the four operand-layout combinations.
+#include <string>
 #include <vector>
 
 #include "sgemm_kernel.h"
@@ -8,13 +9,38 @@ namespace fp32gemm {
 
 const GemmConfig *gemm_configs(int *count) {
   // Built once (thread-safe static initialisation), read-only afterwards.
-  static const std::vector<GemmConfig> table = [] {
-    std::vector<GemmConfig> t = {
-#define FP32GEMM_ROW(BM, BN, BK, WM, WN, OCC) \
-  {#BM "x" #BN "x" #BK "_w" #WM "x" #WN, BM, BN, BK, WM, WN, OCC, {nullptr, nullptr, nullptr, nullptr}},
+  // Names: BMxBNxBK_wWMxWN, then _k2 when two wave groups split K and _s3 /
+  // _s4 for three or four LDS buffers.
+  struct Shape {
+    int bm, bn, bk, wm, wn, ks, s, occ;
+  };
+  static const std::vector<std::string> names = [] {
+    const Shape shapes[] = {
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, S, OCC) {BM, BN, BK, WM, WN, KS, S, OCC},
         FP32GEMM_TILES(FP32GEMM_ROW)
 #undef FP32GEMM_ROW
     };
+    std::vector<std::string> n;
+    for (const Shape &t : shapes) {
+      std::string s = std::to_string(t.bm) + "x" + std::to_string(t.bn) + "x" + std::to_string(t.bk) +
+                      "_w" + std::to_string(t.wm) + "x" + std::to_string(t.wn);
+      if (t.ks > 1) s += "_k" + std::to_string(t.ks);
+      if (t.s > 2) s += "_s" + std::to_string(t.s);
+      n.push_back(s);
+    }
+    return n;
+  }();
+  static const std::vector<GemmConfig> table = [] {
+    const Shape shapes[] = {
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, S, OCC) {BM, BN, BK, WM, WN, KS, S, OCC},
+        FP32GEMM_TILES(FP32GEMM_ROW)
+#undef FP32GEMM_ROW
+    };
+    std::vector<GemmConfig> t;
+    for (size_t i = 0; i < names.size(); ++i) {
+      const Shape &h = shapes[i];
+      t.push_back({names[i].c_str(), h.bm, h.bn, h.bk, h.wm, h.wn, h.occ, {nullptr, nullptr, nullptr, nullptr}});
+    }
     std::vector<GemmLaunchFn> nn(t.size()), nt(t.size()), tn(t.size()), tt(t.size());
     launchers_nn(nn.data());
     launchers_nt(nt.data());

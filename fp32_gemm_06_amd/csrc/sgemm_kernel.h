@@ -22,6 +22,11 @@
 //    LDS buffers and one barrier per slice (double buffering, "11. 探索未尽与
 //    总结"; the two-barrier rule of "GPU GEMM 优化完全拆解（一）", section
 //    "分块的思想");
+//  * optionally (KS = 2) two groups of waves split every K slice between them
+//    and add their accumulators through LDS at the end, in group order: the
+//    pages' split-K ("CUDA 矩阵乘法优化", section "10. cuBLAS 领先的性能差
+//    异") kept inside the workgroup, so small grids get twice the waves per
+//    SIMD without a workspace or any cross-workgroup synchronisation;
 //  * tiles that overhang M, N or K are zero-filled by buffer loads whose
 //    out-of-range offsets read zero, and stores outside C are dropped the same
 //    way ("GPU 基础原理", section "最后一个考虑：分块的量化"), so interior and
@@ -46,15 +51,24 @@
 namespace fp32gemm {
 namespace {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+// KS groups of WT waves each; group g takes MFMA step groups
+// [g * NG / KS, (g + 1) * NG / KS) of every K slice (NG = BK / 8 groups of
+// four MFMA steps).
+// S LDS buffers: on the 128-bit path slice k + S - 1 is in flight while the
+// matrix cores work on slice k (the 32-bit staged path always uses two).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int KS_ = 1, int S_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KS = KS_, S = S_;
   static constexpr int WAVES_N = BN / WN;
-  static constexpr int WAVES = (BM / WM) * WAVES_N;
+  static constexpr int WT = (BM / WM) * WAVES_N;  // waves per K group
+  static constexpr int WAVES = WT * KS;
   static constexpr int NT = WAVES * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int NGW = BK / 8 / KS;  // step groups per wave per slice
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
   static_assert(BK == 16 || BK == 32, "K slice of 16 or 32");
+  static_assert(KS >= 1 && NGW >= 2 && NGW % 2 == 0, "fragment double buffering needs an even group count");
+  static_assert(S >= 2 && S <= 4, "two to four LDS buffers");
 };
 
 // Chunk swizzle of row r of a KC tile (float4 chunks of a BK-float row).
@@ -64,6 +78,18 @@ template <int BK>
 __device__ __forceinline__ int kc_swizzle(int r) {
   if constexpr (BK == 32) return (r & 7) ^ ((r >> 3) & 1);
   else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// Wait until at most VM of this wave's vector-memory instructions are still
+// in flight and its LDS operations are done, then the workgroup barrier.  The
+// barrier carries no memory fence: a fence would make the compiler wait for
+// every DMA still writing LDS (vmcnt(0)), which defeats a deeper pipeline.
+// The "memory" clobber keeps the compiler from moving LDS or buffer accesses
+// across it.
+template <int VM>
+__device__ __forceinline__ void dma_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 // One operand tile: `E` rows or columns along m/n (BM for A, BN for B) by BK
@@ -114,7 +140,8 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   using OA = Operand<KCA, BM, BK, WAVES>;
   using OB = Operand<KCB, BN, BK, WAVES>;
   constexpr int STAGE = OA::FLOATS + OB::FLOATS;
-  __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+  constexpr int NS = DMA ? T::S : 2;  // LDS buffers
+  __shared__ __attribute__((aligned(16))) float lds[NS * STAGE];
 
   // ---- batch and C tile (XCD-aware order) ---------------------------------
   // Workgroups are handed to the 8 XCDs round-robin by id; renumber them so
@@ -140,13 +167,16 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int kg = wave / T::WT, wt = wave % T::WT;  // K group; wave inside the group
+  const int wm = wt / T::WAVES_N, wn = wt % T::WAVES_N;
   const int l32 = lane & 31, half = lane >> 5;
 
   const int rows = a.M - m0;  // valid rows of this tile (may exceed BM)
   const int cols = a.N - n0;
-  const int nk = (a.K + BK - 1) / BK;
-  const int ktail = a.K - (nk - 1) * BK;  // valid k in the last slice, 1..BK
+  // split-K chunks: the last one may be shorter
+  const int Kb = a.k_total > 0 ? min(a.K, a.k_total - (int)bz * a.K) : a.K;
+  const int nk = (Kb + BK - 1) / BK;
+  const int ktail = Kb - (nk - 1) * BK;  // valid k in the last slice, 1..BK
 
   // Source offset (bytes from the slice's base) of the first of this lane's
   // 4 floats per instruction, or kOob when the lane's storage row lies
@@ -305,8 +335,8 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   // buffer just before the barrier).  Fragments are read one group of four
   // MFMA steps ahead; the last group's MFMAs run after the barrier, so they
   // cover the first LDS reads of the next slice.
-  constexpr int NG = BK / 8;
-  static_assert(NG % 2 == 0, "fragment double buffering needs an even group count");
+  constexpr int NGW = T::NGW;
+  const int g0 = kg * NGW;  // this wave's first step group of a slice
   Frag f0, f1;
   auto slice = [&](const float *cur, float *nxt, int kt) {
     const bool more = kt + 1 < nk;
@@ -315,31 +345,100 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
       fetch(nxt, kt + 1);
     }
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int g = 0; g < NGW; ++g) {
       Frag &fc = (g & 1) ? f1 : f0;
       Frag &fn = (g & 1) ? f0 : f1;
-      if (g + 1 < NG) {
-        read_frag(cur, g + 1, fn);
+      if (g + 1 < NGW) {
+        read_frag(cur, g0 + g + 1, fn);
         mma(fc);
       } else {
         if (more) commit(nxt);
         if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
         __syncthreads();
-        if (more) read_frag(nxt, 0, fn);
+        if (more) read_frag(nxt, g0, fn);
         mma(fc);
       }
     }
   };
 
-  set_offsets(nk == 1 ? ktail : BK);
-  fetch(lds, 0);
-  commit(lds);
-  if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  read_frag(lds, 0, f0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int c = kt & 1;
-    slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
+  if constexpr (NS == 2) {
+    set_offsets(nk == 1 ? ktail : BK);
+    fetch(lds, 0);
+    commit(lds);
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    read_frag(lds, g0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int c = kt & 1;
+      slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
+    }
+  } else {
+    // NS - 1 slices in flight.  Every slice issues one fetch, also past the
+    // end of K (all offsets out of range: the DMA writes zeros into a buffer
+    // nobody reads again), so each wave always has exactly (NS - 2) slices'
+    // DMA instructions younger than the slice it waits for, and the wait is a
+    // constant vmcnt.
+    constexpr int NL = OA::NI + OB::NI;          // DMA instructions per wave per slice
+    constexpr int VM = (NS - 2) * NL;            // younger instructions still in flight
+    auto fetch_slice = [&](int ks) {
+      if (ks == nk - 1) set_offsets(ktail);
+      else if (ks == nk) set_offsets(0);
+      fetch(lds + (ks % NS) * STAGE, ks);
+    };
+    set_offsets(BK);
+#pragma unroll
+    for (int ks = 0; ks < NS - 1; ++ks) fetch_slice(ks);
+    dma_barrier<VM>();
+    read_frag(lds, g0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const float *cur = lds + (kt % NS) * STAGE;
+      const float *nxt = lds + ((kt + 1) % NS) * STAGE;
+      fetch_slice(kt + NS - 1);
+#pragma unroll
+      for (int g = 0; g < NGW; ++g) {
+        Frag &fc = (g & 1) ? f1 : f0;
+        Frag &fn = (g & 1) ? f0 : f1;
+        if (g + 1 < NGW) {
+          read_frag(cur, g0 + g + 1, fn);
+          mma(fc);
+        } else {
+          dma_barrier<VM>();  // slice kt + 1 landed (every wave waited for its own part)
+          if (kt + 1 < nk) read_frag(nxt, g0, fn);
+          mma(fc);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the over-fetch has landed before LDS is reused
+    __syncthreads();
+  }
+
+  // ---- K groups: groups 1.. park their sums in LDS, group 0 adds them -----
+  // The last slice ended with a barrier after every LDS read of the loop, so
+  // the buffers are free.  Layout: [group - 1][wave in group][block][v][lane].
+  if constexpr (T::KS > 1) {
+    constexpr int PER = T::TM * T::TN * 16 * 64;  // floats per wave
+    static_assert((T::KS - 1) * T::WT * PER <= 2 * STAGE, "K-group sums fit in the LDS buffers");
+    if (kg > 0) {
+      float *red = lds + ((kg - 1) * T::WT + wt) * PER + lane;
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[((i * T::TN + j) * 16 + v) * 64] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 1; q < T::KS; ++q) {
+      const float *red = lds + ((q - 1) * T::WT + wt) * PER + lane;
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] += red[((i * T::TN + j) * 16 + v) * 64];
+    }
   }
 
   // ---- epilogue: C = alpha * acc + beta * C -------------------------------
@@ -400,18 +499,20 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
 }  // namespace fp32gemm
 
 // The tile shapes the tuning sweep chooses from, in configuration order:
-// (BM, BN, BK, WM, WN, workgroups per CU of the 128-bit path).  Each fits the
-// gfx950 limits (LDS <= 160 KB per workgroup, <= 512 registers per lane); the
-// occupancy column comes from the compiler's LDS and register counts.
-#define FP32GEMM_TILES(X)            \
-  X(256, 256, 32, 128, 64, 1)       \
-  X(256, 256, 16, 128, 64, 1)       \
-  X(256, 128, 32, 64, 64, 1)        \
-  X(128, 256, 32, 64, 64, 1)        \
-  X(128, 128, 32, 64, 32, 2)        \
-  X(256, 128, 32, 128, 64, 1)       \
-  X(256, 128, 16, 128, 64, 1)       \
-  X(128, 256, 32, 64, 128, 1)       \
-  X(128, 128, 32, 64, 64, 2)        \
-  X(128, 128, 16, 64, 64, 3)        \
-  X(64, 64, 32, 32, 32, 4)
+// (BM, BN, BK, WM, WN, K groups, LDS buffers of the 128-bit path, workgroups
+// per CU of the 128-bit path).  Each fits the gfx950 limits (LDS <= 160 KB
+// per workgroup, <= 512 registers per lane); the occupancy column comes from
+// the compiler's LDS and register counts.
+#define FP32GEMM_TILES(X)                  \
+  X(256, 256, 32, 128, 64, 1, 2, 1)       \
+  X(256, 256, 16, 128, 64, 1, 2, 1)       \
+  X(256, 128, 32, 64, 64, 1, 2, 1)        \
+  X(128, 256, 32, 64, 64, 1, 2, 1)        \
+  X(128, 128, 32, 64, 32, 1, 2, 2)        \
+  X(256, 128, 32, 128, 64, 1, 2, 1)       \
+  X(256, 128, 16, 128, 64, 1, 2, 1)       \
+  X(128, 256, 32, 64, 128, 1, 2, 1)       \
+  X(128, 128, 32, 64, 64, 1, 2, 2)        \
+  X(128, 128, 16, 64, 64, 1, 2, 3)        \
+  X(64, 64, 32, 32, 32, 1, 2, 4)          \
+  X(64, 64, 32, 32, 32, 2, 3, 3)

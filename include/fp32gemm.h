@@ -44,6 +44,8 @@
 #ifndef FP32GEMM_H
 #define FP32GEMM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -119,6 +121,44 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K,
                           long long strideB, float beta, float *C, int ldc,
                           long long strideC, int batch_count,
                           fp32gemm_stream_t stream);
+
+/*
+ * Split-K: the same product as sgemm_ex, computed as `splits` partial
+ * products over consecutive chunks of K that run as one grid, then added in
+ * ascending chunk order (so results are bit-reproducible) with alpha and
+ * beta applied once.  This is the K split of "CUDA 矩阵乘法优化：从朴素
+ * Kernel 到接近 cuBLAS", section "10. cuBLAS 领先的性能差异", for shapes
+ * whose C has too few tiles to fill the GPU but whose K is long.
+ *
+ * splits = 0 lets the library choose (fp32gemm_splitk_splits); otherwise
+ * 1 <= splits <= 65535, rounded so that every chunk is a multiple of 32
+ * values of K (the call may use fewer chunks than asked).  With one chunk,
+ * or M <= 8, the call is exactly sgemm_ex and needs no workspace.
+ *
+ * workspace: device memory owned by the caller, at least
+ * sgemm_splitk_workspace_size(M, N, K, splits) bytes, 16-byte aligned for
+ * the fastest path; it holds the partial products (chunks x M x N floats,
+ * packed) between the two kernels, must not overlap A, B or C, and must not
+ * be used by another call until this one has completed on its stream.  The
+ * library allocates nothing.
+ *
+ * Argument positions for error codes: transA 1, transB 2, M 3, N 4, K 5,
+ * alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12, ldc 13, splits 14,
+ * workspace 15 (NULL when needed), workspace_bytes 16 (too small),
+ * stream 17.
+ */
+int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha,
+                 const float *A, int lda, const float *B, int ldb, float beta,
+                 float *C, int ldc, int splits, float *workspace,
+                 size_t workspace_bytes, fp32gemm_stream_t stream);
+
+/* Workspace bytes sgemm_splitk needs for this shape and splits (0 = the
+ * library's choice); 0 when the call runs as a single chunk. */
+size_t sgemm_splitk_workspace_size(int M, int N, int K, int splits);
+
+/* The number of K chunks sgemm_splitk uses with splits = 0: a model of the
+ * tiled kernel's rate for the enlarged grid plus the reduction's traffic. */
+int fp32gemm_splitk_splits(int M, int N, int K);
 
 /* Human-readable text for a return code (static storage, never NULL). */
 const char *fp32gemm_strerror(int code);

@@ -155,3 +155,44 @@ def test_tuned_shapes_resolve_to_their_table_entries(lib):
         for M, N, K, name in re.findall(r'\{(\d+), (\d+), (\d+), "([^"]+)"\}', part):
             cfg = fg.fp32gemm_select_config(fam, int(M), int(N), int(K))
             assert fg.fp32gemm_config_name(fam, cfg) == name, (M, N, K, name)
+
+
+SK = dict(ta=0, tb=0, M=64, N=64, K=4096, alpha=1.0, A=16, lda=4096, B=16, ldb=64, beta=0.0,
+          C=16, ldc=64, splits=4, ws=None, wsb=0)
+
+
+def call_sk(**kw):
+    a = dict(SK, **kw)
+    return fg.sgemm_splitk(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                           a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["splits"],
+                           a["ws"], a["wsb"], 0)
+
+
+def test_splitk_argument_checks_need_no_gpu(lib):
+    assert call_sk(ta=3) == -1
+    assert call_sk(K=-1) == -5
+    assert call_sk(lda=100) == -8
+    assert call_sk(splits=-1) == -14
+    assert call_sk(splits=70000) == -14
+    assert call_sk() == -15                       # four chunks need a workspace
+    assert call_sk(ws=16, wsb=4 * 64 * 64 * 4 - 1) == -16
+    assert call_sk(M=0, A=None, B=None, C=None) == 0
+    assert call_sk(alpha=0.0, beta=1.0, A=None, B=None) == 0
+
+
+def test_splitk_workspace_size(lib):
+    ws = fg.sgemm_splitk_workspace_size
+    assert ws(64, 64, 4096, 4) == 4 * 64 * 64 * 4
+    # 100 / 4 = 25, rounded up to a 32-value chunk: ceil(100 / 32) = 4 chunks
+    assert ws(64, 64, 100, 4) == 4 * 64 * 64 * 4
+    assert ws(64, 64, 96, 4) == 3 * 64 * 64 * 4   # chunks of 32: three of them
+    assert ws(64, 64, 32, 4) == 0                 # one chunk: no workspace
+    assert ws(8, 64, 4096, 4) == 0                # M <= 8 runs the GEMV kernel
+    assert ws(64, 64, 4096, 1) == 0
+    assert ws(64, 64, 4096, -1) == 0
+    # the automatic choice: none for a grid that fills the GPU, several for
+    # a small C with a long K, and the size follows the chosen count
+    assert fg.fp32gemm_splitk_splits(4096, 4096, 4096) == 1
+    s = fg.fp32gemm_splitk_splits(256, 256, 32768)
+    assert s >= 8
+    assert ws(256, 256, 32768, 0) == s * 256 * 256 * 4

@@ -50,6 +50,21 @@ def test_integers_every_config_ragged():
             assert_bitexact(got, ref, f"int {(M, N, K)} {fg.fp32gemm_config_name(0, cfg)}")
 
 
+def test_integers_every_config_short_k_128bit_path():
+    """Aligned shapes (the 128-bit DMA path) with K from one slice to five:
+    the deeper-pipelined tiles fetch up to three slices ahead, so these cover
+    prefetches that start past the end of K and ragged last slices."""
+    require_gpu()
+    for K in (4, 28, 32, 36, 64, 68, 96, 100, 132):
+        M, N = 136, 196
+        A, B, C0 = inputs.random_case(900 + K, M, N, K, kind="int")
+        ref = oracle.sgemm(A, B, C0, 1.0, 0.5)
+        for cfg in range(fg.fp32gemm_num_configs(0)):
+            got, canary = run_hip(A, B, C0, 1.0, 0.5, config=cfg, family="gemm", guard=64)
+            assert canary, f"write outside C, K={K} {fg.fp32gemm_config_name(0, cfg)}"
+            assert_bitexact(got, ref, f"int K={K} {fg.fp32gemm_config_name(0, cfg)}")
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5])
 @pytest.mark.parametrize("shape", [(128, 128), (300, 260), (4092, 4092)], ids=str)
 def test_identity_b(shape, beta):

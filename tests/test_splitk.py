@@ -1,0 +1,157 @@
+"""Split-K (sgemm_splitk) against the CPU oracle.
+
+The partial products over K chunks and their fixed-order sum must give the
+same C as the definition: bit-exact for integer entries (every partial sum is
+an exact integer), within the standard tolerance for uniform entries.  Cases
+cover several chunk counts with a ragged last chunk, all four operand
+layouts, both reduction paths (128-bit and scalar), the automatic choice,
+writes outside C or the workspace, and determinism.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import fp32_gemm_06_amd as fg
+import oracle
+from fp32_gemm_06_amd import inputs
+from gpu_util import assert_bitexact, assert_parity, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 4321.0
+GUARD = 64
+
+
+def _dev(torch, mat, ld, offset):
+    """Device copy of `mat` with row stride ld, `offset` floats past a
+    16-byte boundary, GUARD sentinel floats on both sides, NaN row padding."""
+    r, c = mat.shape
+    flat = torch.full((offset + 2 * GUARD + max(r * ld, 1),), SENTINEL, dtype=torch.float32)
+    v = flat[GUARD + offset: GUARD + offset + r * ld].view(r, ld) if r else None
+    if r:
+        v[:, :c] = torch.from_numpy(mat)
+        if ld > c:
+            v[:, c:] = float("nan")
+    return flat.cuda(), GUARD + offset
+
+
+def run_splitk(ta, tb, A, B, C0, alpha, beta, splits, pads=(0, 0, 0), offset=0, ws_offset=0):
+    """A, B, C0: the op() operands as host arrays.  Returns (C as float64,
+    whether every float outside C and outside the workspace is untouched,
+    the number of chunks used)."""
+    torch = require_gpu()
+    M, K = A.shape
+    N = B.shape[1]
+    a_st = np.ascontiguousarray(A.T) if ta else A
+    b_st = np.ascontiguousarray(B.T) if tb else B
+    lda, ldb, ldc = a_st.shape[1] + pads[0], b_st.shape[1] + pads[1], N + pads[2]
+    dA, oa = _dev(torch, a_st, lda, offset)
+    dB, ob = _dev(torch, b_st, ldb, offset)
+    dC, oc = _dev(torch, C0, ldc, offset)
+    wsb = fg.sgemm_splitk_workspace_size(M, N, K, splits)
+    nws = wsb // 4
+    dW = torch.full((nws + 2 * GUARD + ws_offset,), SENTINEL, dtype=torch.float32, device="cuda")
+    pw = dW.data_ptr() + 4 * (GUARD + ws_offset)
+    rc = fg.sgemm_splitk(ta, tb, M, N, K, alpha, dA.data_ptr() + 4 * oa, lda,
+                         dB.data_ptr() + 4 * ob, ldb, beta, dC.data_ptr() + 4 * oc, ldc, splits,
+                         pw if wsb else None, wsb)
+    if rc:
+        raise fg.Fp32GemmError(rc)
+    torch.cuda.synchronize()
+    host = dC.cpu().numpy()
+    got = host[oc: oc + M * ldc].reshape(M, ldc)[:, :N].astype(np.float64)
+    ok = bool(np.all(host[:oc] == SENTINEL) and np.all(host[oc + M * ldc:] == SENTINEL))
+    if ldc > N:
+        ok = ok and bool(np.all(np.isnan(host[oc: oc + M * ldc].reshape(M, ldc)[:, N:])))
+    w = dW.cpu().numpy()
+    ok = ok and bool(np.all(w[:GUARD + ws_offset] == SENTINEL) and
+                     np.all(w[GUARD + ws_offset + nws:] == SENTINEL))
+    chunks = nws // (M * N) if nws else 1
+    return got, ok, chunks
+
+
+def _ints(seed, M, N, K):
+    g = inputs.rng(seed)
+    return tuple(g.integers(-4, 5, size=s).astype(np.float32) for s in ((M, K), (K, N), (M, N)))
+
+
+@pytest.mark.parametrize("ta,tb", list(itertools.product((0, 1), (0, 1))))
+@pytest.mark.parametrize("shape,splits", [((100, 132, 1000), 3), ((257, 255, 777), 5),
+                                          ((64, 64, 4096), 16), ((300, 260, 130), 4),
+                                          ((96, 200, 4100), 7)], ids=str)
+def test_bitexact(ta, tb, shape, splits):
+    M, N, K = shape
+    A, B, C0 = _ints(M + N + K + 10 * ta + 20 * tb, M, N, K)
+    got, ok, chunks = run_splitk(ta, tb, A, B, C0, 1.0, 0.5, splits, pads=(4, 0, 3))
+    assert chunks > 1
+    assert ok, "write outside C or the workspace"
+    assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"op {ta}{tb} {shape} splits={splits}")
+
+
+@pytest.mark.parametrize("offset,ws_offset", [(1, 0), (0, 1), (3, 2)])
+def test_scalar_paths(offset, ws_offset):
+    """Misaligned operands (32-bit tile loads) and a misaligned workspace or
+    C (scalar reduction); alpha and beta other than 1 and 0."""
+    M, N, K = 130, 98, 999
+    A, B, C0 = _ints(offset * 7 + ws_offset, M, N, K)
+    got, ok, chunks = run_splitk(0, 0, A, B, C0, 2.0, -1.0, 4, offset=offset, ws_offset=ws_offset)
+    assert chunks == 4 and ok
+    assert_bitexact(got, oracle.sgemm(A, B, C0, 2.0, -1.0), f"offsets {offset} {ws_offset}")
+
+
+def test_beta_zero_ignores_nan_c():
+    M, N, K = 64, 96, 2048
+    A, B, _ = _ints(5, M, N, K)
+    C0 = np.full((M, N), np.nan, np.float32)
+    got, ok, _ = run_splitk(0, 1, A, B, C0, 1.0, 0.0, 8)
+    assert ok
+    assert_bitexact(got, oracle.sgemm(A, B, None, 1.0, 0.0), "beta = 0 over NaN")
+
+
+@pytest.mark.parametrize("shape", [(1024, 1024, 16384), (256, 256, 32768), (512, 4096, 4096)],
+                         ids=str)
+def test_auto_splits_uniform(shape):
+    M, N, K = shape
+    g = inputs.rng(M + K)
+    A, B, C0 = inputs.uniform(g, (M, K)), inputs.uniform(g, (K, N)), inputs.uniform(g, (M, N))
+    got, ok, chunks = run_splitk(0, 0, A, B, C0, 0.75, 0.5, 0)
+    assert ok
+    assert chunks == fg.fp32gemm_splitk_splits(M, N, K)
+    if M * N * K <= 1 << 32:
+        ref, bnd = oracle.sgemm(A, B, C0, 0.75, 0.5), oracle.bound(A, B, C0, 0.75, 0.5)
+        assert_parity(got, ref, bnd, f"auto {shape}")
+    else:
+        rows = np.array([0, 1, M // 2, M - 1], dtype=np.int32)
+        rr = np.repeat(rows, N).astype(np.int32)
+        cc = np.tile(np.arange(N, dtype=np.int32), len(rows))
+        ref = oracle.sgemm_entries(rr, cc, A, B, C0, 0.75, 0.5)
+        bnd = oracle.bound_entries(rr, cc, A, B, C0, 0.75, 0.5)
+        assert_parity(got[rr, cc], ref, bnd, f"auto {shape} sampled")
+
+
+def test_single_chunk_and_small_m_need_no_workspace():
+    """One chunk (short K) or M <= 8 run the plain routine."""
+    for (M, N, K) in [(100, 100, 32), (5, 300, 4096)]:
+        A, B, C0 = _ints(M * K, M, N, K)
+        assert fg.sgemm_splitk_workspace_size(M, N, K, 8) == 0
+        got, ok, chunks = run_splitk(0, 1, A, B, C0, 1.0, 0.5, 8)
+        assert chunks == 1 and ok
+        assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"{(M, N, K)} single chunk")
+
+
+def test_deterministic():
+    torch = require_gpu()
+    M, N, K = 256, 384, 8192
+    g = inputs.rng(77)
+    A = torch.from_numpy(inputs.uniform(g, (M, K))).cuda()
+    B = torch.from_numpy(inputs.uniform(g, (K, N))).cuda()
+    wsb = fg.sgemm_splitk_workspace_size(M, N, K, 0)
+    W = torch.empty(wsb // 4, device="cuda")
+    outs = []
+    for _ in range(3):
+        C = torch.zeros(M, N, device="cuda")
+        assert fg.sgemm_splitk(0, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N, 0, W, wsb) == 0
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
