@@ -127,16 +127,31 @@ def sweep(out_path: str, reps: int, warm: int, only: str | None):
             torch.cuda.empty_cache()
 
 
+# SGEMM near-ties: tile-ordering groups of one tile shape often time within
+# the sweep's noise of each other, but a larger group shares more A and B
+# panels in each XCD's L2 (at 4092^3, group 8 fetched 407 MB per launch from
+# the fabric against 603 MB for group 2, for the same time).  Within this
+# fraction of the fastest time the largest group of the fastest tile wins.
+TIE = 0.005
+
+
 def best_by_shape(path: str):
-    best = {}
+    rows = {}
     with open(path) as f:
         for ln in f:
             if not ln.strip():
                 continue
             r = json.loads(ln)
-            k = (r["family"], r["M"], r["N"], r["K"])
-            if k not in best or r["us"] < best[k]["us"]:
-                best[k] = r
+            rows.setdefault((r["family"], r["M"], r["N"], r["K"]), []).append(r)
+    best = {}
+    for k, rs in rows.items():
+        b = min(rs, key=lambda r: r["us"])
+        if k[0] == "gemm":
+            tile = b["config"].rsplit("_g", 1)[0]
+            near = [r for r in rs if r["config"].rsplit("_g", 1)[0] == tile
+                    and r["us"] <= b["us"] * (1 + TIE)]
+            b = max(near, key=lambda r: int(r["config"].rsplit("_g", 1)[1]))
+        best[k] = b
     return best
 
 
