@@ -13,6 +13,10 @@ alpha times the inner product of row i of A with column j of B, plus beta
 times the old C.  See ``oracle.c`` for the readings taken where the pages are
 silent (leading dimensions, beta == 0 / alpha == 0, rounding).
 
+The fused variants (``sgemm_fused`` and friends) add a per-column bias and
+an optional ReLU after the update: the operator-fusion example of "GPU 基础
+原理", section "4.1 算子融合" (y = relu(x + 1)), applied to a GEMM output.
+
 Every function here is pinned by ``tests/test_oracle.py`` against exact
 rational arithmetic on tiny inputs, closed forms (identity and all-ones
 operands), exact integer products, linearity in alpha/beta and the
@@ -54,6 +58,9 @@ def _bind(lib):
     lib.oracle_bound_entries.argtypes = lib.oracle_sgemm_entries.argtypes
     for f in (lib.oracle_sgemm, lib.oracle_bound, lib.oracle_sgemm_entries, lib.oracle_bound_entries):
         f.restype = None
+    lib.oracle_epilogue.argtypes = [ctypes.c_int, _I32P, _I32P, _F32P, ctypes.c_int, _F64P,
+                                    _F64P]
+    lib.oracle_epilogue.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     return lib
 
@@ -159,6 +166,65 @@ def bound_entries(rows, cols, A, B, C0=None, alpha: float = 1.0, beta: float = 0
     lib = lib or load()
     K = A.shape[1] if K is None else K
     return _entries(lib.oracle_bound_entries, rows, cols, A, B, C0, alpha, beta, K)
+
+
+ACT_NONE = 0
+ACT_RELU = 1
+
+
+def _epilogue(lib, vals, rows, cols, bias, act, bnd=None):
+    """Apply the fused epilogue (oracle_epilogue) in place to float64 arrays."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
+    cols = np.ascontiguousarray(cols, dtype=np.int32).ravel()
+    if not vals.flags.c_contiguous:
+        raise ValueError("epilogue values must be C-contiguous")
+    flat = vals.reshape(-1)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    bp = None if b is None else b.ctypes.data_as(_F32P)
+    lib.oracle_epilogue(flat.size, rows.ctypes.data_as(_I32P), cols.ctypes.data_as(_I32P), bp,
+                        int(act), flat.ctypes.data_as(_F64P),
+                        None if bnd is None else bnd.reshape(-1).ctypes.data_as(_F64P))
+
+
+def sgemm_fused(A, B, C0=None, alpha: float = 1.0, beta: float = 0.0, bias=None,
+                act: int = ACT_NONE, M=None, N=None, K=None, lib=None) -> np.ndarray:
+    """Reference act(alpha A B + beta C0 + bias[None, :]) in float64 (bias: one
+    float32 per column of C, or None; act: ACT_NONE or ACT_RELU)."""
+    lib = lib or load()
+    out = sgemm(A, B, C0, alpha, beta, M=M, N=N, K=K, lib=lib)
+    rr, cc = np.indices(out.shape, dtype=np.int32)
+    _epilogue(lib, out, rr, cc, bias, act)
+    return out
+
+
+def bound_fused(A, B, C0=None, alpha: float = 1.0, beta: float = 0.0, bias=None, M=None,
+                N=None, K=None, lib=None) -> np.ndarray:
+    """Tolerance scale of sgemm_fused: bound(...) + |bias[j]|."""
+    lib = lib or load()
+    bnd = bound(A, B, C0, alpha, beta, M=M, N=N, K=K, lib=lib)
+    vals = np.zeros_like(bnd)
+    rr, cc = np.indices(bnd.shape, dtype=np.int32)
+    _epilogue(lib, vals, rr, cc, bias, ACT_NONE, bnd)
+    return bnd
+
+
+def sgemm_fused_entries(rows, cols, A, B, C0=None, alpha: float = 1.0, beta: float = 0.0,
+                        bias=None, act: int = ACT_NONE, K=None, lib=None) -> np.ndarray:
+    """sgemm_fused at the selected elements only."""
+    lib = lib or load()
+    out = sgemm_entries(rows, cols, A, B, C0, alpha, beta, K=K, lib=lib)
+    _epilogue(lib, out, rows, cols, bias, act)
+    return out
+
+
+def bound_fused_entries(rows, cols, A, B, C0=None, alpha: float = 1.0, beta: float = 0.0,
+                        bias=None, K=None, lib=None) -> np.ndarray:
+    """bound_fused at the selected elements only."""
+    lib = lib or load()
+    bnd = bound_entries(rows, cols, A, B, C0, alpha, beta, K=K, lib=lib)
+    vals = np.zeros_like(bnd)
+    _epilogue(lib, vals, rows, cols, bias, ACT_NONE, bnd)
+    return bnd
 
 
 def threads(lib=None) -> int:

@@ -33,6 +33,9 @@
  * The bound array Bnd = |alpha| * (|A| |B|) + |beta| * |C0| is what the
  * acceptance test scales its tolerance by.
  *
+ * oracle_epilogue adds the fused bias + activation of the pages' operator
+ * fusion example (see its comment) to those results.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math: the order of the
  * double sum must stay as written).
  */
@@ -183,6 +186,45 @@ void oracle_bound_entries(int count, const int *rows, const int *cols, int K,
     }
     if (beta != 0.0f) s += bb * fabs((double)C0[i * ldc + j]);
     out[t] = s;
+  }
+}
+
+/*
+ * Fused epilogue, applied to values the functions above produced.  The pages
+ * fuse an elementwise chain into the kernel that produces its input ("GPU
+ * 基础原理", section "4.1 算子融合": y = relu(x + 1) in one pass, the
+ * intermediate never stored); on a GEMM output the chain is a linear layer's
+ * epilogue:
+ *
+ *   vals[t] <- act(vals[t] + bias[cols[t]])
+ *
+ * with one bias value per column of C (NULL = no bias) and act 0 = identity,
+ * 1 = ReLU: v < 0 gives 0, anything else (including NaN and -0.0) passes
+ * unchanged.  The bias is added in double, then the activation is applied.
+ * bnd[t] (may be NULL) receives + |bias[cols[t]]|, the matching tolerance
+ * scale; ReLU moves two values no further apart, so it adds nothing.
+ * rows[] is unused by the faithful oracle (the bias does not depend on the
+ * row).
+ */
+void oracle_epilogue(int count, const int *rows, const int *cols, const float *bias, int act,
+                     double *vals, double *bnd) {
+  (void)rows;
+  for (int t = 0; t < count; ++t) {
+#if ORACLE_MUTANT == 5 /* bias indexed by the row */
+    const double b = bias ? (double)bias[rows[t]] : 0.0;
+#else
+    const double b = bias ? (double)bias[cols[t]] : 0.0;
+#endif
+    double v = vals[t];
+#if ORACLE_MUTANT == 6 /* activation before the bias */
+    if (act == 1 && v < 0.0) v = 0.0;
+    v += b;
+#else
+    v += b;
+    if (act == 1 && v < 0.0) v = 0.0;
+#endif
+    vals[t] = v;
+    if (bnd) bnd[t] += fabs(b);
   }
 }
 

@@ -14,7 +14,11 @@ What pins what:
   * linearity in alpha and beta;
   * transpose identity (A B)^T = B^T A^T;
   * leading dimensions: NaN-padded rows give the packed result;
-  * the read conventions for beta == 0, alpha == 0 and K == 0.
+  * the read conventions for beta == 0, alpha == 0 and K == 0;
+  * the fused epilogue (bias + ReLU): a hand-worked example, the bias axis
+    (alpha = beta = 0 leaves the bias in every row), the exact identity
+    relu(v) - relu(-v) = v under negation of alpha, beta and the bias, the
+    bound, NaN/inf handling, and entries against the full result.
 """
 from __future__ import annotations
 
@@ -167,5 +171,83 @@ def pin_read_conventions(lib):
     assert np.array_equal(got, -C0.astype(np.float64)), "K == 0 gives beta C0"
 
 
+# ---- fused epilogue: act(alpha A B + beta C0 + bias[j]) -------------------
+
+def pin_epilogue_worked_example(lib):
+    """By hand: A = [1 2 3], B columns (1, 0, -1) and (0, 1, -1), so
+    A B = [1 - 3, 2 - 3] = [-2, -1]."""
+    A = np.array([[1, 2, 3]], np.float32)
+    B = np.array([[1, 0], [0, 1], [-1, -1]], np.float32)
+    bias = np.array([1, 5], np.float32)
+    # [-2 + 1, -1 + 5] = [-1, 4]; ReLU clears the negative one
+    assert np.array_equal(oracle.sgemm_fused(A, B, None, 1.0, 0.0, bias, 0, lib=lib), [[-1, 4]])
+    assert np.array_equal(oracle.sgemm_fused(A, B, None, 1.0, 0.0, bias, 1, lib=lib), [[0, 4]])
+    # with C0 = [3, -10], beta = 1/2: [-2 + 1.5 + 1, -1 - 5 + 5] = [0.5, -1]
+    C0 = np.array([[3, -10]], np.float32)
+    assert np.array_equal(oracle.sgemm_fused(A, B, C0, 1.0, 0.5, bias, 1, lib=lib), [[0.5, 0]])
+    assert np.array_equal(oracle.sgemm_fused(A, B, C0, 1.0, 0.5, None, 1, lib=lib), [[0, 0]])
+    # tolerance scale: |A||B| = [1 + 3, 2 + 3], plus |bias|
+    assert np.array_equal(oracle.bound_fused(A, B, None, 1.0, 0.0, -bias, lib=lib), [[5, 10]])
+
+
+def pin_epilogue_bias_axis(lib):
+    """alpha = beta = 0 leaves act(bias[j]) in every row: one bias value per
+    column of C, the same for all rows."""
+    M, N, K = 3, 5, 4
+    bias = np.array([-2.5, 1.0, 0.0, 7.0, -0.25], np.float32)
+    A, B, _ = inputs.random_case(61, M, N, K, kind="int")
+    for act, want in ((0, bias.astype(np.float64)), (1, np.array([0, 1, 0, 7, 0], np.float64))):
+        got = oracle.sgemm_fused(A, B, None, 0.0, 0.0, bias, act, lib=lib)
+        assert np.array_equal(got, np.tile(want, (M, 1))), ("bias axis", act)
+
+
+def pin_epilogue_relu_identity(lib):
+    """relu(v) - relu(-v) = v exactly, and negating alpha, beta and the bias
+    negates v: the ReLU results at (alpha, beta, bias) and (-alpha, -beta,
+    -bias) must differ by the identity-activation result.  Integer data keep
+    every value exact; the identity result minus the plain product is the
+    bias, row by row; ReLU results are never negative."""
+    M, N, K = 6, 7, 9
+    A, B, C0 = inputs.random_case(62, M, N, K, kind="int")
+    bias = inputs.rng(63).integers(-30, 31, size=N).astype(np.float32)
+    for alpha, beta in ((1.0, 0.5), (-2.0, 1.0), (3.0, 0.0)):
+        lin = oracle.sgemm_fused(A, B, C0, alpha, beta, bias, 0, lib=lib)
+        pos = oracle.sgemm_fused(A, B, C0, alpha, beta, bias, 1, lib=lib)
+        neg = oracle.sgemm_fused(A, B, C0, -alpha, -beta, -bias, 1, lib=lib)
+        assert np.array_equal(pos - neg, lin), ("relu identity", alpha, beta)
+        assert np.all(pos >= 0), "relu result negative"
+        plain = oracle.sgemm(A, B, C0, alpha, beta, lib=lib)
+        assert np.array_equal(lin - plain, np.tile(bias.astype(np.float64), (M, 1))), "bias add"
+        bnd = oracle.bound_fused(A, B, C0, alpha, beta, bias, lib=lib)
+        assert np.array_equal(bnd - oracle.bound(A, B, C0, alpha, beta, lib=lib),
+                              np.tile(np.abs(bias).astype(np.float64), (M, 1))), "bound"
+
+
+def pin_epilogue_special_values(lib):
+    """NaN passes through the ReLU (it is not below zero); -inf becomes 0."""
+    A = np.zeros((2, 1), np.float32)
+    B = np.zeros((1, 2), np.float32)
+    C0 = np.array([[np.nan, -np.inf], [np.inf, -0.0]], np.float32)
+    got = oracle.sgemm_fused(A, B, C0, 1.0, 1.0, None, 1, lib=lib)
+    assert np.isnan(got[0, 0]) and got[0, 1] == 0.0 and got[1, 0] == np.inf and got[1, 1] == 0.0
+
+
+def pin_epilogue_entries(lib):
+    M, N, K = 9, 11, 5
+    A, B, C0 = inputs.random_case(64, M, N, K, kind="uniform")
+    bias = inputs.uniform(inputs.rng(65), (N,))
+    rows = np.array([0, 3, 8, 8, 5], np.int32)
+    cols = np.array([10, 0, 4, 10, 7], np.int32)
+    for act in (0, 1):
+        full = oracle.sgemm_fused(A, B, C0, 1.5, -0.5, bias, act, lib=lib)
+        ent = oracle.sgemm_fused_entries(rows, cols, A, B, C0, 1.5, -0.5, bias, act, lib=lib)
+        assert np.array_equal(ent, full[rows, cols]), ("entries", act)
+    bfull = oracle.bound_fused(A, B, C0, 1.5, -0.5, bias, lib=lib)
+    bent = oracle.bound_fused_entries(rows, cols, A, B, C0, 1.5, -0.5, bias, lib=lib)
+    assert np.array_equal(bent, bfull[rows, cols]), "bound entries"
+
+
 ALL_PINS = [pin_bruteforce, pin_identity, pin_ones, pin_integers, pin_linearity,
-            pin_transpose, pin_leading_dims, pin_read_conventions]
+            pin_transpose, pin_leading_dims, pin_read_conventions,
+            pin_epilogue_worked_example, pin_epilogue_bias_axis, pin_epilogue_relu_identity,
+            pin_epilogue_special_values, pin_epilogue_entries]

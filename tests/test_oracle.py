@@ -15,8 +15,9 @@ def test_pin(pin, oracle_lib):
 
 # Planted mistakes compiled into separate copies of the oracle (CPU only):
 # 1 drops the last k term, 2 reads B transposed, 3 flips the sign of the
-# beta term, 4 ignores the leading dimension of C0.
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4])
+# beta term, 4 ignores the leading dimension of C0, 5 indexes the epilogue's
+# bias by row, 6 applies the ReLU before adding the bias.
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6])
 def test_pins_catch_planted_mistake(mutant):
     with tempfile.TemporaryDirectory() as d:
         path = oracle.build(os.path.join(d, f"liboracle_m{mutant}.so"), mutant=mutant)
