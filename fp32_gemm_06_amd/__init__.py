@@ -37,11 +37,14 @@ _BATCHED_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, cty
                      ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
                      ctypes.c_void_p]
 
+_FUSED_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+ACT_NONE = 0
+ACT_RELU = 1
 _SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
 
 # Every symbol include/fp32gemm.h declares.
-EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_splitk",
+EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_fused", "sgemm_splitk",
            "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits", "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
            "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
@@ -68,6 +71,8 @@ def lib():
         L.sgemm_ex.restype = ctypes.c_int
         L.sgemm_strided_batched.argtypes = _BATCHED_ARGTYPES
         L.sgemm_strided_batched.restype = ctypes.c_int
+        L.sgemm_fused.argtypes = _FUSED_ARGTYPES
+        L.sgemm_fused.restype = ctypes.c_int
         L.sgemm_splitk.argtypes = _SPLITK_ARGTYPES
         L.sgemm_splitk.restype = ctypes.c_int
         L.sgemm_splitk_workspace_size.argtypes = [ctypes.c_int] * 4
@@ -132,6 +137,14 @@ def sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ld
     return lib().sgemm_strided_batched(transA, transB, M, N, K, alpha, _addr(A), lda, strideA,
                                        _addr(B), ldb, strideB, beta, _addr(C), ldc, strideC,
                                        batch_count, _stream(stream))
+
+
+def sgemm_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                stream=None) -> int:
+    """C <- act(alpha op(A) op(B) + beta C + bias[None, :]); bias may be None,
+    act is ACT_NONE or ACT_RELU."""
+    return lib().sgemm_fused(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                             _addr(C), ldc, _addr(bias), act, _stream(stream))
 
 
 def sgemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,

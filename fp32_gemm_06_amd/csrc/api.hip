@@ -58,7 +58,8 @@ int quick_return(const GemmArgs &a, hipStream_t s, int *rc) {
     return 1;
   }
   if (a.alpha == 0.0f || a.K == 0) {
-    *rc = (a.beta == 1.0f) ? 0 : (int)launch_scale(a, s);
+    const bool noop = a.beta == 1.0f && a.bias == nullptr && a.act == kActNone;
+    *rc = noop ? 0 : (int)launch_scale(a, s);
     return 1;
   }
   return 0;
@@ -91,6 +92,8 @@ GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const f
   a.sA = a.sB = a.sC = 0;
   a.batch = 1;
   a.k_total = 0;
+  a.bias = nullptr;
+  a.act = kActNone;
   return a;
 }
 
@@ -147,6 +150,22 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alp
   if (batch_count > 65535) return -kPosBatched.batch;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
+  return run_gemm(-1, transA, transB, a, s);
+}
+
+int sgemm_fused(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
+                fp32gemm_stream_t stream) {
+  GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemmEx, transA, transB, a);
+  if (rc) return rc;
+  if (act != FP32GEMM_ACT_NONE && act != FP32GEMM_ACT_RELU) return -15;
+  a.bias = bias;
+  a.act = act == FP32GEMM_ACT_RELU ? kActRelu : kActNone;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quick_return(a, s, &rc)) return rc;
+  if (gemv_supported(a, transA))
+    return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
   return run_gemm(-1, transA, transB, a, s);
 }
 

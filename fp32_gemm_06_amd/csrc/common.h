@@ -23,7 +23,20 @@ struct GemmArgs {
   // [b * K, min((b + 1) * K, k_total)) of the whole product (its operands are
   // already offset by sA, sB); 0 for ordinary calls.
   int k_total;
+  // Fused epilogue: C[i][j] = act(alpha acc + beta C0 + bias[j]); bias may be
+  // NULL (no bias), act is kActNone or kActRelu.
+  const float *bias;
+  int act;
 };
+
+constexpr int kActNone = 0;
+constexpr int kActRelu = 1;
+
+// The activation of the fused epilogue: ReLU maps v < 0 to 0 and passes
+// everything else (NaN and -0.0 included) unchanged.
+__device__ __forceinline__ float apply_act(float v, int act) {
+  return (act == kActRelu && v < 0.0f) ? 0.0f : v;
+}
 
 // Buffer-resource word 3 for gfx9-family raw buffers: 32-bit data format,
 // no swizzle, no index stride.  With a raw resource a load whose byte offset

@@ -441,9 +441,11 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     }
   }
 
-  // ---- epilogue: C = alpha * acc + beta * C -------------------------------
+  // ---- epilogue: C = act(alpha * acc + beta * C + bias[col]) ----------------
   // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32 of its 32 x 32 block.
+  // column l%32 of its 32 x 32 block.  The bias and the activation are the
+  // fused elementwise chain of "GPU 基础原理", section "4.1 算子融合",
+  // applied in registers before the only store of C.
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(Cg + (size_t)m0 * a.ldc + n0);
   const float alpha = a.alpha, beta = a.beta;
   auto c_off = [&](int i, int j, int v) -> uint32_t {
@@ -451,6 +453,21 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     const int col = wn * T::WN + j * 32 + l32;
     return (row < rows && col < cols) ? (uint32_t)(row * a.ldc + col) * 4u : kOob;
   };
+  float bj[T::TN];  // this lane's bias value per 32-column block
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) bj[j] = 0.0f;
+  if (a.bias != nullptr) {
+    const __amdgpu_buffer_rsrc_t rs_bias = make_rsrc(a.bias + n0);
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int col = wn * T::WN + j * 32 + l32;
+      const uint32_t off = col < cols ? (uint32_t)col * 4u : kOob;
+      bj[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_bias, off, 0, 0));
+    }
+  }
+  const bool fused = a.bias != nullptr || a.act != kActNone;
+  const int act = a.act;
+  auto finish = [&](float out, int j) -> float { return fused ? apply_act(out + bj[j], act) : out; };
   if (beta != 0.0f) {
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
@@ -462,7 +479,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
           c0[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_c, c_off(i, j, v), 0, 0));
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float out = alpha * acc[i][j][v] + beta * c0[v];
+          const float out = finish(alpha * acc[i][j][v] + beta * c0[v], j);
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
         }
       }
@@ -473,7 +490,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
       for (int j = 0; j < T::TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float out = alpha * acc[i][j][v];
+          const float out = finish(alpha * acc[i][j][v], j);
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
         }
   }

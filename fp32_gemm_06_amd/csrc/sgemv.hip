@@ -179,7 +179,8 @@ sgemv_kernel(GemmArgs a, int transA) {
     float *y = a.C + (size_t)m * a.ldc + n0 + c;
     float out = alpha * s;
     if (beta != 0.0f) out += beta * *y;
-    *y = out;
+    if (a.bias) out += a.bias[n0 + c];
+    *y = apply_act(out, a.act);
   }
 }
 
@@ -329,7 +330,8 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
     float *y = a.C + (size_t)m * a.ldc + n;
     float out = a.alpha * sum;
     if (a.beta != 0.0f) out += a.beta * *y;
-    *y = out;
+    if (a.bias) out += a.bias[n];
+    *y = apply_act(out, a.act);
   }
 }
 
@@ -377,13 +379,17 @@ namespace {
 // C <- beta * C for every batch entry (blockIdx.z); beta == 0 stores zeros
 // without reading C.
 __global__ void __launch_bounds__(256)
-scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta) {
+scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta, const float *bias,
+             int act) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= N) return;
   float *Cz = C + (long long)blockIdx.z * sC;
+  const float bj = bias ? bias[j] : 0.0f;
   for (int i = blockIdx.y; i < M; i += gridDim.y) {
     float *p = Cz + (size_t)i * ldc + j;
-    *p = (beta == 0.0f) ? 0.0f : beta * *p;
+    float v = (beta == 0.0f) ? 0.0f : beta * *p;
+    if (bias) v += bj;
+    *p = apply_act(v, act);
   }
 }
 
@@ -438,7 +444,8 @@ const GemvConfig *gemv_configs(int *count) {
 hipError_t launch_scale(const GemmArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 1024 ? a.M : 1024),
                   (unsigned)a.batch);
-  hipLaunchKernelGGL(scale_kernel, grid, dim3(256), 0, s, a.C, a.M, a.N, a.ldc, a.sC, a.beta);
+  hipLaunchKernelGGL(scale_kernel, grid, dim3(256), 0, s, a.C, a.M, a.N, a.ldc, a.sC, a.beta,
+                     a.bias, a.act);
   return hipGetLastError();
 }
 

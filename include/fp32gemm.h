@@ -123,6 +123,30 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K,
                           fp32gemm_stream_t stream);
 
 /*
+ * Fused epilogue: C[i][j] <- act(alpha * (op(A) op(B))[i][j] + beta * C[i][j]
+ * + bias[j]), operands as in sgemm_ex.  This is the operator fusion of "GPU
+ * 基础原理" (a translation of "Basic facts about GPUs"), section "4.1 算子融合":
+ * the elementwise chain (the page's example is y = relu(x + 1)) runs on the
+ * product in registers, so C is stored once instead of being written, read
+ * and written again by separate kernels.
+ *
+ * bias: device pointer to N floats, one per column of C (a linear layer's
+ * output features), owned by the caller; NULL = no bias.  act:
+ * FP32GEMM_ACT_NONE or FP32GEMM_ACT_RELU (v < 0 becomes 0; NaN and -0.0 pass
+ * unchanged).  The bias is added first, then the activation is applied.
+ * alpha = 0 or K = 0 still applies the epilogue to beta * C.  Routing as in
+ * sgemm_ex (M <= 8 takes a GEMV kernel).  Argument positions for error
+ * codes: as sgemm_ex for 1..13, bias 14, act 15 (unknown activation),
+ * stream 16.
+ */
+#define FP32GEMM_ACT_NONE 0
+#define FP32GEMM_ACT_RELU 1
+int sgemm_fused(int transA, int transB, int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb, float beta,
+                float *C, int ldc, const float *bias, int act,
+                fp32gemm_stream_t stream);
+
+/*
  * Split-K: the same product as sgemm_ex, computed as `splits` partial
  * products over consecutive chunks of K that run as one grid, then added in
  * ascending chunk order (so results are bit-reproducible) with alpha and

@@ -196,3 +196,19 @@ def test_splitk_workspace_size(lib):
     s = fg.fp32gemm_splitk_splits(256, 256, 32768)
     assert s >= 8
     assert ws(256, 256, 32768, 0) == s * 256 * 256 * 4
+
+
+def test_fused_argument_checks_need_no_gpu(lib):
+    def f(**kw):
+        a = dict(EX, bias=None, act=0)
+        a.update(kw)
+        return fg.sgemm_fused(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                              a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["bias"],
+                              a["act"], 0)
+    assert f(act=2) == -15
+    assert f(act=-1) == -15
+    assert f(ta=5) == -1
+    assert f(C=None) == -12
+    assert f(M=0, A=None, B=None, C=None, act=1) == 0
+    # alpha == 0, beta == 1 and no epilogue: C is left alone without a launch
+    assert f(alpha=0.0, beta=1.0, A=None, B=None) == 0
