@@ -66,13 +66,17 @@ const char *gemm_config_name(int id) {
 
 // Fallback for shapes the table does not list.  The pages observe that a grid
 // with too few blocks leaves the GPU idle ("CUDA 矩阵乘法优化", section
-// "10. cuBLAS 领先的性能差异").  The estimate per tile shape is its full-load
-// rate on MI355X (measured by the sweep) times its wave-quantization
-// efficiency over the 256 CUs (tiles / (rounds * 256), one 8-wave workgroup
-// per CU reaching full rate), and for the 4-wave 64x64 tile a further factor
-// for fewer than four workgroups per CU.  Checked against the sweep, the
-// estimate picks the measured best tile at 1536^3, 2048^3, 3072^3, 512x4096
-// and 512x11008, and is within about 10% of the measured rate elsewhere.
+// "10. cuBLAS 领先的性能差异"), and that edge tiles waste the part of the
+// tile outside the matrix ("GPU 基础原理", section "最后一个考虑：分块的量化").
+// The estimate per tile shape is its full-load rate on MI355X (measured by
+// the sweep) scaled by the useful fraction of the work: each of the rounds
+// of up to 256 tiles (one 8-wave workgroup per CU at full rate) costs a whole
+// tile's work, of which M x N of the rounds' tile area is useful.  The 4-wave
+// 64x64 tile gets a further factor for fewer than four workgroups per CU,
+// which stops falling at one per CU (256 tiles).  Checked against the sweep,
+// the estimate picks the measured best of the three tiles at 15 of the 16
+// swept shapes (at 2048^3 the two it confuses are 1.7% apart); tiny shapes
+// such as 128^3 get the 64x64 tile.
 int model_gemm_config(int M, int N, int mult, double *rate_out) {
   struct Candidate {
     const char *name;
@@ -90,8 +94,9 @@ int model_gemm_config(int M, int N, int mult, double *rate_out) {
   for (const Candidate &c : cands) {
     const double tiles = (double)((M + c.bm - 1) / c.bm) * (double)((N + c.bn - 1) / c.bn) * mult;
     const double rounds = (double)(long long)((tiles + 255.0) / 256.0);
-    double rate = c.full_rate * tiles / (rounds * 256.0);
-    if (c.small && tiles < 1024.0) rate *= pow(tiles / 1024.0, 0.3);
+    // each round costs a whole tile's work per CU; only M x N x mult of it is useful
+    double rate = c.full_rate / 256.0 * ((double)M * (double)N * mult) / (rounds * c.bm * c.bn);
+    if (c.small && tiles < 1024.0) rate *= pow((tiles < 256.0 ? 256.0 : tiles) / 1024.0, 0.3);
     const int id = find_gemm(c.name);
     if (id >= 0 && rate > best_rate) {
       best_rate = rate;
@@ -104,13 +109,17 @@ int model_gemm_config(int M, int N, int mult, double *rate_out) {
 
 // Fallback for shapes the table does not list.  The pages observe that a grid
 // with too few blocks leaves the GPU idle ("CUDA 矩阵乘法优化", section
-// "10. cuBLAS 领先的性能差异").  The estimate per tile shape is its full-load
-// rate on MI355X (measured by the sweep) times its wave-quantization
-// efficiency over the 256 CUs (tiles / (rounds * 256), one 8-wave workgroup
-// per CU reaching full rate), and for the 4-wave 64x64 tile a further factor
-// for fewer than four workgroups per CU.  Checked against the sweep, the
-// estimate picks the measured best tile at 1536^3, 2048^3, 3072^3, 512x4096
-// and 512x11008, and is within about 10% of the measured rate elsewhere.
+// "10. cuBLAS 领先的性能差异"), and that edge tiles waste the part of the
+// tile outside the matrix ("GPU 基础原理", section "最后一个考虑：分块的量化").
+// The estimate per tile shape is its full-load rate on MI355X (measured by
+// the sweep) scaled by the useful fraction of the work: each of the rounds
+// of up to 256 tiles (one 8-wave workgroup per CU at full rate) costs a whole
+// tile's work, of which M x N of the rounds' tile area is useful.  The 4-wave
+// 64x64 tile gets a further factor for fewer than four workgroups per CU,
+// which stops falling at one per CU (256 tiles).  Checked against the sweep,
+// the estimate picks the measured best of the three tiles at 15 of the 16
+// swept shapes (at 2048^3 the two it confuses are 1.7% apart); tiny shapes
+// such as 128^3 get the 64x64 tile.
 int select_gemm_config(int M, int N, int K) {
   for (const ShapeEntry &e : kGemmTable)
     if (e.M == M && e.N == N && e.K == K) {
