@@ -9,14 +9,14 @@ namespace fp32gemm {
 
 const GemmConfig *gemm_configs(int *count) {
   // Built once (thread-safe static initialisation), read-only afterwards.
-  // Names: BMxBNxBK_wWMxWN, then _k2 when two wave groups split K and _s3 /
-  // _s4 for three or four LDS buffers.
+  // Names: BMxBNxBK_wWMxWN, then _k2 when two wave groups split K and _p2 /
+  // _p4 for K slices per barrier.
   struct Shape {
-    int bm, bn, bk, wm, wn, ks, s, occ;
+    int bm, bn, bk, wm, wn, ks, p, occ;
   };
   static const std::vector<std::string> names = [] {
     const Shape shapes[] = {
-#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, S, OCC) {BM, BN, BK, WM, WN, KS, S, OCC},
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC) {BM, BN, BK, WM, WN, KS, P, OCC},
         FP32GEMM_TILES(FP32GEMM_ROW)
 #undef FP32GEMM_ROW
     };
@@ -25,14 +25,14 @@ const GemmConfig *gemm_configs(int *count) {
       std::string s = std::to_string(t.bm) + "x" + std::to_string(t.bn) + "x" + std::to_string(t.bk) +
                       "_w" + std::to_string(t.wm) + "x" + std::to_string(t.wn);
       if (t.ks > 1) s += "_k" + std::to_string(t.ks);
-      if (t.s > 2) s += "_s" + std::to_string(t.s);
+      if (t.p > 1) s += "_p" + std::to_string(t.p);
       n.push_back(s);
     }
     return n;
   }();
   static const std::vector<GemmConfig> table = [] {
     const Shape shapes[] = {
-#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, S, OCC) {BM, BN, BK, WM, WN, KS, S, OCC},
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC) {BM, BN, BK, WM, WN, KS, P, OCC},
         FP32GEMM_TILES(FP32GEMM_ROW)
 #undef FP32GEMM_ROW
     };

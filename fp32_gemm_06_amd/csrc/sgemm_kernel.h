@@ -54,11 +54,12 @@ namespace {
 // KS groups of WT waves each; group g takes MFMA step groups
 // [g * NG / KS, (g + 1) * NG / KS) of every K slice (NG = BK / 8 groups of
 // four MFMA steps).
-// S LDS buffers: on the 128-bit path slice k + S - 1 is in flight while the
-// matrix cores work on slice k (the 32-bit staged path always uses two).
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int KS_ = 1, int S_ = 2>
+// P > 1 (128-bit path): P K slices per barrier, i.e. stages of P slices in
+// 2 P LDS buffers, the next stage in flight during the current one (the
+// 32-bit staged path always uses one slice per barrier).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int KS_ = 1, int P_ = 1>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KS = KS_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KS = KS_, P = P_;
   static constexpr int WAVES_N = BN / WN;
   static constexpr int WT = (BM / WM) * WAVES_N;  // waves per K group
   static constexpr int WAVES = WT * KS;
@@ -68,7 +69,7 @@ struct Tile {
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
   static_assert(BK == 16 || BK == 32, "K slice of 16 or 32");
   static_assert(KS >= 1 && NGW >= 2 && NGW % 2 == 0, "fragment double buffering needs an even group count");
-  static_assert(S >= 2 && S <= 4, "two to four LDS buffers");
+  static_assert(P >= 1 && P <= 4, "one to four K slices per barrier");
 };
 
 // Chunk swizzle of row r of a KC tile (float4 chunks of a BK-float row).
@@ -78,18 +79,6 @@ template <int BK>
 __device__ __forceinline__ int kc_swizzle(int r) {
   if constexpr (BK == 32) return (r & 7) ^ ((r >> 3) & 1);
   else return ((r >> 1) ^ (r >> 3)) & 3;
-}
-
-// Wait until at most VM of this wave's vector-memory instructions are still
-// in flight and its LDS operations are done, then the workgroup barrier.  The
-// barrier carries no memory fence: a fence would make the compiler wait for
-// every DMA still writing LDS (vmcnt(0)), which defeats a deeper pipeline.
-// The "memory" clobber keeps the compiler from moving LDS or buffer accesses
-// across it.
-template <int VM>
-__device__ __forceinline__ void dma_barrier() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 // One operand tile: `E` rows or columns along m/n (BM for A, BN for B) by BK
@@ -140,7 +129,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   using OA = Operand<KCA, BM, BK, WAVES>;
   using OB = Operand<KCB, BN, BK, WAVES>;
   constexpr int STAGE = OA::FLOATS + OB::FLOATS;
-  constexpr int NS = DMA ? T::S : 2;  // LDS buffers
+  constexpr int NS = DMA ? 2 * T::P : 2;  // LDS buffers
   __shared__ __attribute__((aligned(16))) float lds[NS * STAGE];
 
   // ---- batch and C tile (XCD-aware order) ---------------------------------
@@ -361,7 +350,55 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
-  if constexpr (NS == 2) {
+  if constexpr (DMA && T::P > 1) {
+    // P slices per barrier.  Stage st is slices [st P, st P + P) in buffers
+    // (st % 2) P .. (st % 2) P + P - 1.  The next stage's P fetches start at
+    // the top of a stage (past the end of K they are masked: zeros into a
+    // free buffer, and those slices then add exact zeros); at the end of the
+    // stage every wave waits for its own DMA and one barrier publishes the
+    // whole next stage.  Within a stage the last group of a slice reads the
+    // first group of the next slice without a barrier (it has landed).
+    constexpr int P = T::P;
+    auto fetch_slice = [&](int ks) {
+      if (ks == nk - 1) set_offsets(ktail);
+      else if (ks == nk) set_offsets(0);
+      fetch(lds + (ks % (2 * P)) * STAGE, ks);
+    };
+    const int nst = (nk + P - 1) / P;
+    set_offsets(BK);
+#pragma unroll
+    for (int u = 0; u < P; ++u) fetch_slice(u);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    read_frag(lds, g0, f0);
+    for (int st = 0; st < nst; ++st) {
+      float *base = lds + (st & 1) * P * STAGE;
+      float *nbase = lds + ((st + 1) & 1) * P * STAGE;
+#pragma unroll
+      for (int u = 0; u < P; ++u) fetch_slice((st + 1) * P + u);
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const float *cur = base + u * STAGE;
+#pragma unroll
+        for (int g = 0; g < NGW; ++g) {
+          Frag &fc = (g & 1) ? f1 : f0;
+          Frag &fn = (g & 1) ? f0 : f1;
+          if (g + 1 < NGW) {
+            read_frag(cur, g0 + g + 1, fn);
+            mma(fc);
+          } else if (u + 1 < P) {
+            read_frag(cur + STAGE, g0, fn);
+            mma(fc);
+          } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next stage of this wave landed
+            __syncthreads();
+            if (st + 1 < nst) read_frag(nbase, g0, fn);
+            mma(fc);
+          }
+        }
+      }
+    }
+  } else {
     set_offsets(nk == 1 ? ktail : BK);
     fetch(lds, 0);
     commit(lds);
@@ -372,44 +409,6 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
       const int c = kt & 1;
       slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
     }
-  } else {
-    // NS - 1 slices in flight.  Every slice issues one fetch, also past the
-    // end of K (all offsets out of range: the DMA writes zeros into a buffer
-    // nobody reads again), so each wave always has exactly (NS - 2) slices'
-    // DMA instructions younger than the slice it waits for, and the wait is a
-    // constant vmcnt.
-    constexpr int NL = OA::NI + OB::NI;          // DMA instructions per wave per slice
-    constexpr int VM = (NS - 2) * NL;            // younger instructions still in flight
-    auto fetch_slice = [&](int ks) {
-      if (ks == nk - 1) set_offsets(ktail);
-      else if (ks == nk) set_offsets(0);
-      fetch(lds + (ks % NS) * STAGE, ks);
-    };
-    set_offsets(BK);
-#pragma unroll
-    for (int ks = 0; ks < NS - 1; ++ks) fetch_slice(ks);
-    dma_barrier<VM>();
-    read_frag(lds, g0, f0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const float *cur = lds + (kt % NS) * STAGE;
-      const float *nxt = lds + ((kt + 1) % NS) * STAGE;
-      fetch_slice(kt + NS - 1);
-#pragma unroll
-      for (int g = 0; g < NGW; ++g) {
-        Frag &fc = (g & 1) ? f1 : f0;
-        Frag &fn = (g & 1) ? f0 : f1;
-        if (g + 1 < NGW) {
-          read_frag(cur, g0 + g + 1, fn);
-          mma(fc);
-        } else {
-          dma_barrier<VM>();  // slice kt + 1 landed (every wave waited for its own part)
-          if (kt + 1 < nk) read_frag(nxt, g0, fn);
-          mma(fc);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the over-fetch has landed before LDS is reused
-    __syncthreads();
   }
 
   // ---- K groups: groups 1.. park their sums in LDS, group 0 adds them -----
@@ -516,20 +515,22 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
 }  // namespace fp32gemm
 
 // The tile shapes the tuning sweep chooses from, in configuration order:
-// (BM, BN, BK, WM, WN, K groups, LDS buffers of the 128-bit path, workgroups
-// per CU of the 128-bit path).  Each fits the gfx950 limits (LDS <= 160 KB
-// per workgroup, <= 512 registers per lane); the occupancy column comes from
-// the compiler's LDS and register counts.
-#define FP32GEMM_TILES(X)                  \
-  X(256, 256, 32, 128, 64, 1, 2, 1)       \
-  X(256, 256, 16, 128, 64, 1, 2, 1)       \
-  X(256, 128, 32, 64, 64, 1, 2, 1)        \
-  X(128, 256, 32, 64, 64, 1, 2, 1)        \
-  X(128, 128, 32, 64, 32, 1, 2, 2)        \
-  X(256, 128, 32, 128, 64, 1, 2, 1)       \
-  X(256, 128, 16, 128, 64, 1, 2, 1)       \
-  X(128, 256, 32, 64, 128, 1, 2, 1)       \
-  X(128, 128, 32, 64, 64, 1, 2, 2)        \
-  X(128, 128, 16, 64, 64, 1, 2, 3)        \
-  X(64, 64, 32, 32, 32, 1, 2, 4)          \
-  X(64, 64, 32, 32, 32, 2, 3, 3)
+// (BM, BN, BK, WM, WN, K groups, K slices per barrier of the 128-bit path,
+// workgroups per CU of the 128-bit path).  Each fits the gfx950 limits (LDS
+// <= 160 KB per workgroup, <= 512 registers per lane); the occupancy column
+// comes from the compiler's LDS and register counts.
+#define FP32GEMM_TILES(X)             \
+  X(256, 256, 32, 128, 64, 1, 1, 1)  \
+  X(256, 256, 16, 128, 64, 1, 1, 1)  \
+  X(256, 128, 32, 64, 64, 1, 1, 1)   \
+  X(128, 256, 32, 64, 64, 1, 1, 1)   \
+  X(128, 128, 32, 64, 32, 1, 1, 2)   \
+  X(256, 128, 32, 128, 64, 1, 1, 1)  \
+  X(256, 128, 16, 128, 64, 1, 1, 1)  \
+  X(128, 256, 32, 64, 128, 1, 1, 1)  \
+  X(128, 128, 32, 64, 64, 1, 1, 2)   \
+  X(128, 128, 16, 64, 64, 1, 1, 3)   \
+  X(64, 64, 32, 32, 32, 1, 1, 4)     \
+  X(64, 64, 32, 32, 32, 1, 2, 2)     \
+  X(64, 64, 32, 32, 32, 1, 4, 1)     \
+  X(64, 64, 32, 32, 32, 2, 2, 2)
