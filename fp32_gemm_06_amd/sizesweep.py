@@ -24,6 +24,7 @@ def main():
     ap.add_argument("--sizes", type=int, nargs="*", default=SIZES)
     ap.add_argument("--ops", nargs="*", default=["nn"], choices=["nn", "nt", "tn", "tt"],
                     help="operand layouts: n = as given, t = stored transposed")
+    ap.add_argument("--md", default=None, help="also write a markdown table here")
     a = ap.parse_args()
 
     import torch
@@ -57,6 +58,7 @@ def main():
     for _ in range(60):
         torch.matmul(big, big)
     del big
+    recs = []
     with open(a.out, "w") as out:
         for n in a.sizes:
             for op in a.ops:
@@ -86,7 +88,16 @@ def main():
                        "config": fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, n, n, n))}
                 print(json.dumps(rec), flush=True)
                 out.write(json.dumps(rec) + "\n")
+                recs.append(rec)
                 del A, B, C
+    if a.md:
+        lines = ["| n | op | sgemm us | sgemm TFLOP/s | vendor TFLOP/s | vendor time / ours "
+                 "| max_rel_err | config |", "|---" * 8 + "|"]
+        for r in recs:
+            lines.append(f"| {r['n']} | {r['op']} | {r['us']} | {r['tflops']} | {r['vendor_tflops']} "
+                         f"| {r['ratio']} | {r['max_rel_err']:.1e} | {r['config']} |")
+        with open(a.md, "w") as f:
+            f.write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":
