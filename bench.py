@@ -20,7 +20,6 @@ fp32 matrix peak), "gemv" (decode GEMV bandwidth against HBM peak),
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -37,11 +36,9 @@ GEMV_SOURCES = [os.path.join(ROOT, "fp32_gemm_06_amd", "csrc", f)
 
 
 def source_hash(paths) -> str:
-    h = hashlib.sha256()
-    for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel code (comments excluded), as the profile summaries record it."""
+    from fp32_gemm_06_amd.profiling import source_hash as code_hash
+    return code_hash(paths)
 
 
 def stored_traffic(name: str, paths):

@@ -21,7 +21,8 @@
 //  * slice k+1 is fetched while the matrix cores work on slice k, with two
 //    LDS buffers and one barrier per slice (double buffering, "11. 探索未尽与
 //    总结"; the two-barrier rule of "GPU GEMM 优化完全拆解（一）", section
-//    "分块的思想");
+//    "分块的思想"); small tiles may instead stage P slices per barrier, which
+//    matters when a CU holds a single workgroup;
 //  * optionally (KS = 2) two groups of waves split every K slice between them
 //    and add their accumulators through LDS at the end, in group order: the
 //    pages' split-K ("CUDA 矩阵乘法优化", section "10. cuBLAS 领先的性能差

@@ -19,6 +19,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -33,11 +34,21 @@ CALIB = "neg_kernel"
 CALIB_BYTES = 256 << 20
 
 
+def code_text(path):
+    """A source file without its comments and blank lines: what the compiler
+    sees, so that editing a comment does not invalidate recorded counters."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_hash(files):
+    """Hash of the code (comments excluded) of the named csrc files, or of
+    the given paths when they are absolute."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_text(f if os.path.isabs(f) else os.path.join(CSRC, f)).encode())
     return h.hexdigest()[:16]
 
 
