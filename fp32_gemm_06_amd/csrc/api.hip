@@ -150,6 +150,9 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alp
   if (batch_count > 65535) return -kPosBatched.batch;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
+  if (gemv_supported(a, transA))
+    return transB ? (int)launch_gemv_rows(a, transA, -1, s)
+                  : run_gemv(select_gemv_config_batched(M, N, K, batch_count), transA, a, s);
   return run_gemm(-1, transA, transB, a, s);
 }
 

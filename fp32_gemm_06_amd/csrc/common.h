@@ -133,5 +133,7 @@ int select_gemm_config(int M, int N, int K);
 // chunks); *rate receives the modelled TFLOP/s.
 int model_gemm_config(int M, int N, int mult, double *rate);
 int select_gemv_config(int M, int N, int K);
+// GEMV choice for `batch` products of M x N (the grid is stripes x batch).
+int select_gemv_config_batched(int M, int N, int K, int batch);
 
 }  // namespace fp32gemm

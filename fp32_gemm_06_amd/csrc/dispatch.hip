@@ -129,19 +129,24 @@ int select_gemm_config(int M, int N, int K) {
   return model_gemm_config(M, N, 1, nullptr);
 }
 
-int select_gemv_config(int M, int N, int K) {
-  for (const ShapeEntry &e : kGemvTable)
-    if (e.M == M && e.N == N && e.K == K) {
-      const int id = find_gemv(e.name);
-      if (id >= 0) return id;
-    }
+int select_gemv_config(int M, int N, int K) { return select_gemv_config_batched(M, N, K, 1); }
+
+int select_gemv_config_batched(int M, int N, int K, int batch) {
+  if (batch == 1)
+    for (const ShapeEntry &e : kGemvTable)
+      if (e.M == M && e.N == N && e.K == K) {
+        const int id = find_gemv(e.name);
+        if (id >= 0) return id;
+      }
+  // the workgroup count is the stripes of N times the batch entries
+  const long long NB = (long long)N * (batch > 1 ? batch : 1);
   // Wider column stripes read longer runs of each row of W (64, 128 or 256
   // bytes), which the memory system serves faster, but give fewer
   // workgroups.  The sweep over N from 1024 to 65536 is fastest with the
   // widest stripe that still leaves about 160 workgroups or more.
   (void)K;
-  const char *name = N >= 160 * 64   ? "c64_w8_u4"
-                     : N >= 256 * 32 ? "c32_w8_u4"
+  const char *name = NB >= 160 * 64   ? "c64_w8_u4"
+                     : NB >= 256 * 32 ? "c32_w8_u4"
                      : M >= 4        ? "c16_w4_u8"
                                      : "c16_w8_u4";
   const int id = find_gemv(name);

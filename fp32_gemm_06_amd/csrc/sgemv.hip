@@ -54,6 +54,12 @@ sgemv_kernel(GemmArgs a, int transA) {
   __shared__ __attribute__((aligned(16))) float xs[2][MR][ROWS];
   __shared__ float red[NW][MR][CBW];
 
+  // batch entry (strided batches; 0 for a single product)
+  const long long bz = blockIdx.y;
+  a.A += bz * a.sA;
+  a.B += bz * a.sB;
+  a.C += bz * a.sC;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,29 +208,42 @@ sgemv_kernel(GemmArgs a, int transA) {
 constexpr int kRowsWaves = 4;
 constexpr int kRowsThreads = kRowsWaves * 64;
 
-template <int MR, bool VEC, int RW>
+template <int MR, bool VEC, int RW, int LPR, int CH>
 __global__ void __launch_bounds__(kRowsThreads)
 sgemv_rows_kernel(GemmArgs a, int transA) {
-  constexpr int CH = MR <= 4 ? 1024 : 512;   // K floats per chunk
   constexpr int VW = VEC ? 4 : 1;            // weight floats per lane per position
-  constexpr int STEP = 64 * VW;              // k covered by one wave instruction
+  constexpr int RPI = 64 / LPR;              // rows per wave instruction
+  constexpr int STEP = LPR * VW;             // k covered by one lane group per instruction
   constexpr int POS = CH / STEP;             // positions per chunk
-  constexpr int XPT = MR * CH / kRowsThreads;  // X floats staged per thread per chunk
+  constexpr int XN = MR * CH;                // X values staged per chunk
+  constexpr int XPT = (XN + kRowsThreads - 1) / kRowsThreads;
+  static_assert(64 % LPR == 0 && CH % STEP == 0 && MR * RW <= LPR, "row-dot lane mapping");
   __shared__ __attribute__((aligned(16))) float xs[2][MR * CH];
+
+  // batch entry (strided batches; 0 for a single product)
+  const long long bz = blockIdx.y;
+  a.A += bz * a.sA;
+  a.B += bz * a.sB;
+  a.C += bz * a.sC;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = (blockIdx.x * kRowsWaves + wave) * RW;  // first row of this wave
+  const int slot = lane / LPR, li = lane % LPR;  // row slot of the instruction; lane in it
+  // this wave owns rows nw + r * RPI + slot, r < RW
+  const int nw = (blockIdx.x * kRowsWaves + wave) * RPI * RW;
   const int K = a.K;
   // X element (m, k0 + kk) sits at A + k0 * xk + kk * xk + m * xm
   const uint32_t xk = transA ? (uint32_t)a.lda : 1u, xm = transA ? 1u : (uint32_t)a.lda;
 
-  __amdgpu_buffer_rsrc_t rs[RW];
+  // one buffer base per wave (at its first row); each lane group's row goes
+  // into the offset
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B + (nw < a.N ? (size_t)nw * a.ldb : 0));
   bool live[RW];
+  uint32_t rowoff[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    live[r] = n0 + r < a.N;
-    rs[r] = make_rsrc(a.B + (live[r] ? (size_t)(n0 + r) * a.ldb : 0));
+    live[r] = nw + r * RPI + slot < a.N;
+    rowoff[r] = (uint32_t)(r * RPI + slot) * (uint32_t)a.ldb * 4u;
   }
 
   // weights of the chunk at k0: RW rows x POS positions, zeros past K or N
@@ -233,14 +252,14 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
     for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int p = 0; p < POS; ++p) {
-        const int k = k0 + p * STEP + lane * VW;
-        const uint32_t off = live[r] && k < K ? (uint32_t)k * 4u : kOob;
+        const int k = k0 + p * STEP + li * VW;
+        const uint32_t off = live[r] && k < K ? rowoff[r] + (uint32_t)k * 4u : kOob;
         if constexpr (VEC) {
-          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs[r], off, 0, 0);
+          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[r][p][e] = v[e];
         } else {
-          w[r][p][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs[r], off, 0, 0));
+          w[r][p][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
         }
       }
   };
@@ -251,13 +270,17 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = tid + j * kRowsThreads, m = i / CH, kk = i % CH;
-      const uint32_t off = k0 + kk < K ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
+      const bool ok = (XN % kRowsThreads == 0 || i < XN) && k0 + kk < K;
+      const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
       x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     }
   };
   auto store_x = [&](const float (&x)[XPT], int buf) {
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) xs[buf][tid + j * kRowsThreads] = x[j];
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + j * kRowsThreads;
+      if (XN % kRowsThreads == 0 || i < XN) xs[buf][i] = x[j];
+    }
   };
 
   float acc[MR][RW];
@@ -268,7 +291,7 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
   auto multiply = [&](const float (&w)[RW][POS][VW], int buf) {
 #pragma unroll
     for (int p = 0; p < POS; ++p) {
-      const int k = p * STEP + lane * VW;
+      const int k = p * STEP + li * VW;
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         float x[VW];
@@ -312,21 +335,22 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
     __syncthreads();
   }
 
-  // butterfly over the 64 lanes; lane m * RW + r then writes output (m, n0 + r)
+  // butterfly over the LPR lanes of each row slot; lane li = m * RW + r of
+  // the slot then writes output (m, row nw + r * RPI + slot)
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1)
+  for (int sh = 1; sh < LPR; sh <<= 1)
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-      for (int r = 0; r < RW; ++r) acc[m][r] += __shfl_xor(acc[m][r], s, 64);
+      for (int r = 0; r < RW; ++r) acc[m][r] += __shfl_xor(acc[m][r], sh, 64);
   float sum = 0.0f;
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int r = 0; r < RW; ++r)
-      if (lane == m * RW + r) sum = acc[m][r];
-  const int m = lane / RW, n = n0 + lane % RW;
-  if (lane < MR * RW && n < a.N) {
+      if (li == m * RW + r) sum = acc[m][r];
+  const int m = li / RW, n = nw + (li % RW) * RPI + slot;
+  if (li < MR * RW && n < a.N) {
     float *y = a.C + (size_t)m * a.ldc + n;
     float out = a.alpha * sum;
     if (a.beta != 0.0f) out += a.beta * *y;
@@ -335,14 +359,20 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
   }
 }
 
-template <bool VEC, int RW>
+template <bool VEC, int RW, int LPR, int CH_SHORT>
 hipError_t launch_rows_rw(const GemmArgs &a, int transA, hipStream_t s) {
-  const long long wgs = ((long long)a.N + kRowsWaves * RW - 1) / (kRowsWaves * RW);
-  if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)wgs), block(kRowsThreads);
+  constexpr int RPW = (64 / LPR) * RW;  // rows per wave
+  const long long wgs = ((long long)a.N + kRowsWaves * RPW - 1) / (kRowsWaves * RPW);
+  if (wgs > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)wgs, (unsigned)a.batch), block(kRowsThreads);
+  // K chunk: 1024 (512 for M > 4) with whole-wave rows, CH_SHORT with short rows
   switch (a.M) {
-#define FP32GEMM_ROWS_CASE(MR) \
-  case MR: hipLaunchKernelGGL((sgemv_rows_kernel<MR, VEC, RW>), grid, block, 0, s, a, transA); break;
+#define FP32GEMM_ROWS_CASE(MR)                                                                 \
+  case MR:                                                                                     \
+    hipLaunchKernelGGL((sgemv_rows_kernel<MR, VEC, RW, LPR,                                    \
+                                          LPR == 64 ? (MR <= 4 ? 1024 : 512) : CH_SHORT>),     \
+                       grid, block, 0, s, a, transA);                                          \
+    break;
     FP32GEMM_ROWS_CASE(1)
     FP32GEMM_ROWS_CASE(2)
     FP32GEMM_ROWS_CASE(3)
@@ -365,13 +395,25 @@ bool gemv_supported(const GemmArgs &a, int transA) {
 
 // Rows per wave: one for M <= 3 (the most waves, which keeps the most loads
 // in flight), two from M = 4 on (each staged X value then feeds two rows).
-// A timing sweep over decode shapes (N, K in 1024 .. 32000) picked these.
+// Short rows share a wave instruction, 16 lanes (64 floats per instruction)
+// to a row, with K chunks of 256: a whole wave per row leaves most lanes and
+// most of each chunk masked at small K (K = 128: 57.7 against 15.0 us for
+// 64 MB of weights).  Timing both variants over K from 256 to 2048 put the
+// switch at K = 1024 (M <= 3: whole waves from 1024 on; M >= 4: from 2048).
 hipError_t launch_gemv_rows(const GemmArgs &a, int transA, int rows_per_wave, hipStream_t s) {
   if (!gemv_supported(a, transA)) return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.K % 4 == 0 && a.ldb % 4 == 0;
   const int rw = rows_per_wave > 0 ? rows_per_wave : a.M >= 4 ? 2 : 1;
-  if (vec) return rw >= 2 ? launch_rows_rw<true, 2>(a, transA, s) : launch_rows_rw<true, 1>(a, transA, s);
-  return rw >= 2 ? launch_rows_rw<false, 2>(a, transA, s) : launch_rows_rw<false, 1>(a, transA, s);
+  if (a.K < 1024 || (a.M >= 4 && a.K == 1024)) {
+    if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 16, 256>(a, transA, s)
+                            : launch_rows_rw<true, 1, 16, 256>(a, transA, s);
+    return rw >= 2 ? launch_rows_rw<false, 2, 16, 256>(a, transA, s)
+                   : launch_rows_rw<false, 1, 16, 256>(a, transA, s);
+  }
+  if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 64, 0>(a, transA, s)
+                          : launch_rows_rw<true, 1, 64, 0>(a, transA, s);
+  return rw >= 2 ? launch_rows_rw<false, 2, 64, 0>(a, transA, s)
+                 : launch_rows_rw<false, 1, 64, 0>(a, transA, s);
 }
 
 namespace {
@@ -396,8 +438,8 @@ scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta, const fl
 template <bool VEC, int CBW, int NW, int U>
 hipError_t launch_cfg(const GemmArgs &a, int transA, hipStream_t s) {
   const long long blocks = ((long long)a.N + CBW - 1) / CBW;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(NW * 64);
+  if (blocks > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks, (unsigned)a.batch), block(NW * 64);
   switch (a.M) {
 #define FP32GEMM_GEMV_CASE(MR)                                                                   \
   case MR:                                                                                       \

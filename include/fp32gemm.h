@@ -110,8 +110,9 @@ int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha,
  * strideA or strideB may be 0 (one operand shared by every entry); the C
  * entries must not overlap: strideC >= (M - 1) * ldc + N when
  * batch_count > 1.  Per-head attention products (Q K^T and P V for every
- * head) are this shape.  0 <= batch_count <= 65535; batch_count == 0 does
- * nothing.  Argument positions: transA 1, transB 2, M 3, N 4, K 5, alpha 6,
+ * head) are this shape; with M <= 8 (decode: one query row per head) the
+ * entries run on the GEMV kernels, with one grid over all entries.
+ * 0 <= batch_count <= 65535; batch_count == 0 does nothing.  Argument positions: transA 1, transB 2, M 3, N 4, K 5, alpha 6,
  * A 7, lda 8, strideA 9, B 10, ldb 11, strideB 12, beta 13, C 14, ldc 15,
  * strideC 16, batch_count 17, stream 18.
  */

@@ -98,3 +98,24 @@ def test_deterministic():
         outs.append(C)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 8])
+@pytest.mark.parametrize("K", [64, 128, 200, 500])
+def test_short_rows_share_wave_instructions(M, K):
+    """Rows shorter than 512 floats: four rows per wave instruction (16 lanes
+    each), K chunks of 256; N ragged against the 4 (or 8) rows a wave owns."""
+    N = 301
+    for ta in (0, 1):
+        As, Bs, Cs = _case(8000 + 10 * M + K + ta, M, N, K)
+        (got,), ok = run_batched(ta, 1, As, Bs, Cs, 1.0, 0.5, pads=(2, 4, 3))
+        assert ok, "write outside C"
+        assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"M={M} K={K} ta={ta}")
+
+
+def test_short_rows_scalar_path():
+    M, N, K = 2, 257, 130     # K % 4 != 0: 32-bit weight loads
+    As, Bs, Cs = _case(8100, M, N, K)
+    (got,), ok = run_batched(0, 1, As, Bs, Cs, 2.0, -1.0, offset=1)
+    assert ok
+    assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 2.0, -1.0), "short rows, 32-bit")

@@ -219,3 +219,52 @@ def test_batched_scale_only():
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(C, want)
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_batched_small_m_gemv(ta, tb, M):
+    """M <= 8 entries run on the GEMV kernels (column stripes for op(B) = B,
+    row dots for op(B) = B^T), one grid over the batch: the decode-time
+    attention products (q K^T and p V per head)."""
+    N, K, batch = 300, 500, 5
+    As, Bs, Cs = _case(40 + M + 10 * ta + 20 * tb, M, N, K, batch=batch)
+    outs, ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=(4, 4, 4), gaps=(8, 4, 12))
+    assert ok, "write outside the C entries"
+    for b in range(batch):
+        assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5), f"M={M} entry {b}")
+
+
+def test_batched_decode_attention_shapes():
+    """32 heads, head dimension 128, 2048 cached positions, one query row:
+    scores q K^T (K cache stored positions x dim) and the weighted sum p V."""
+    heads, seq, dim = 32, 2048, 128
+    g = inputs.rng(9)
+    q = [inputs.uniform(g, (1, dim)) for _ in range(heads)]
+    kt = [inputs.uniform(g, (dim, seq)) for _ in range(heads)]       # op(B) = K^T
+    z = [np.zeros((1, seq), np.float32) for _ in range(heads)]
+    outs, ok = run_batched(0, 1, q, kt, z, 0.088, 0.0)
+    assert ok
+    for b in (0, 17, 31):
+        assert_parity(outs[b], oracle.sgemm(q[b], kt[b], None, 0.088, 0.0),
+                      oracle.bound(q[b], kt[b], None, 0.088, 0.0), f"scores head {b}")
+    p = [inputs.uniform(g, (1, seq)) for _ in range(heads)]
+    v = [inputs.uniform(g, (seq, dim)) for _ in range(heads)]
+    z = [np.zeros((1, dim), np.float32) for _ in range(heads)]
+    outs, ok = run_batched(0, 0, p, v, z, 1.0, 0.0)
+    assert ok
+    for b in (0, 17, 31):
+        assert_parity(outs[b], oracle.sgemm(p[b], v[b], None, 1.0, 0.0),
+                      oracle.bound(p[b], v[b], None, 1.0, 0.0), f"p V head {b}")
+
+
+def test_batched_small_m_shared_and_misaligned():
+    """strideA = 0 with M = 2, and odd strides (32-bit loads in the GEMV kernels)."""
+    M, N, K, batch = 2, 77, 301, 4
+    As, Bs, Cs = _case(12, M, N, K, batch=batch)
+    As = [As[0]] * batch
+    for tb in (0, 1):
+        outs, ok = run_batched(0, tb, As, Bs, Cs, 2.0, -1.0, gaps=(0, 1, 3), share_a=True, offset=1)
+        assert ok
+        for b in range(batch):
+            assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 2.0, -1.0), f"tb={tb} {b}")
