@@ -54,25 +54,26 @@ sgemv_kernel(GemmArgs a, int transA) {
   __shared__ __attribute__((aligned(16))) float xs[2][MR][ROWS];
   __shared__ float red[NW][MR][CBW];
 
-  // batch entry (strided batches; 0 for a single product)
-  const long long bz = blockIdx.y;
-  a.A += bz * a.sA;
-  a.B += bz * a.sB;
-  a.C += bz * a.sC;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane / LPR;           // row group inside the wave
   const int cl = (lane % LPR) * VW;   // first column of this lane in the block
 
-  // Column block: workgroups go to the XCDs round-robin by id (XCD = id % 8);
-  // blocks 2j and 2j+1 go to XCD j % 8.  Ids past the last full group of 16
-  // keep their own number.
-  const int G = gridDim.x, bid = blockIdx.x;
-  const int cb = bid < (G & ~15)
-                     ? 2 * (8 * ((bid >> 3) >> 1) + (bid & 7)) + ((bid >> 3) & 1)
-                     : bid;
+  // Work item (batch entry, column block): workgroups go to the XCDs
+  // round-robin by their linear id over the whole grid (XCD = id % 8);
+  // items 2j and 2j+1 (the two stripes of a 128-byte line when CBW = 16) go
+  // to XCD j % 8, so the line is fetched once into that XCD's L2.  Ids past
+  // the last full group of 16 keep their own number.
+  const int G = gridDim.x;
+  const long long L = (long long)blockIdx.y * G + blockIdx.x;
+  const long long T = (long long)gridDim.y * G;
+  const long long w = L < (T & ~15LL) ? 2 * (8 * ((L >> 3) >> 1) + (L & 7)) + ((L >> 3) & 1) : L;
+  const long long bz = w / G;         // batch entry (0 for a single product)
+  const int cb = (int)(w - bz * G);   // column block
+  a.A += bz * a.sA;
+  a.B += bz * a.sB;
+  a.C += bz * a.sC;
   const int n0 = cb * CBW;
   const bool col_ok = n0 + cl < a.N;  // VEC: N % 4 == 0, so the float4 is whole
   const int K = a.K;
