@@ -209,7 +209,7 @@ sgemv_kernel(GemmArgs a, int transA) {
 constexpr int kRowsWaves = 4;
 constexpr int kRowsThreads = kRowsWaves * 64;
 
-template <int MR, bool VEC, int RW, int LPR, int CH>
+template <int MR, bool VEC, int RW, int LPR, int CH, bool XV>
 __global__ void __launch_bounds__(kRowsThreads)
 sgemv_rows_kernel(GemmArgs a, int transA) {
   constexpr int VW = VEC ? 4 : 1;            // weight floats per lane per position
@@ -217,7 +217,8 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
   constexpr int STEP = LPR * VW;             // k covered by one lane group per instruction
   constexpr int POS = CH / STEP;             // positions per chunk
   constexpr int XN = MR * CH;                // X values staged per chunk
-  constexpr int XPT = (XN + kRowsThreads - 1) / kRowsThreads;
+  constexpr int XW = XV ? 4 : 1;             // X values per staging load
+  constexpr int XPT = (XN / XW + kRowsThreads - 1) / kRowsThreads;  // staging loads per thread
   static_assert(64 % LPR == 0 && CH % STEP == 0 && MR * RW <= LPR, "row-dot lane mapping");
   __shared__ __attribute__((aligned(16))) float xs[2][MR * CH];
 
@@ -264,23 +265,33 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
         }
       }
   };
-  // X of the chunk at k0, element i = m * CH + kk for i = tid + j * threads
-  // (consecutive lanes read consecutive k), zeros past K
-  auto load_x = [&](float (&x)[XPT], int k0) {
+  // X of the chunk at k0, elements i .. i + XW - 1 = m * CH + kk .. with
+  // i = XW * (tid + j * threads) (consecutive lanes read consecutive k),
+  // zeros past K.  XV: op(A) = A with 16-byte aligned rows and K % 4 == 0,
+  // so each float4 is all inside or all outside K.
+  auto load_x = [&](floatx4 (&x)[XPT], int k0) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + (size_t)k0 * xk);
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-      const int i = tid + j * kRowsThreads, m = i / CH, kk = i % CH;
-      const bool ok = (XN % kRowsThreads == 0 || i < XN) && k0 + kk < K;
+      const int i = XW * (tid + j * kRowsThreads), m = i / CH, kk = i % CH;
+      const bool ok = (XN % (XW * kRowsThreads) == 0 || i < XN) && k0 + kk < K;
       const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
-      x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+      if constexpr (XV)
+        x[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      else
+        x[j][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     }
   };
-  auto store_x = [&](const float (&x)[XPT], int buf) {
+  auto store_x = [&](const floatx4 (&x)[XPT], int buf) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-      const int i = tid + j * kRowsThreads;
-      if (XN % kRowsThreads == 0 || i < XN) xs[buf][i] = x[j];
+      const int i = XW * (tid + j * kRowsThreads);
+      if (XN % (XW * kRowsThreads) == 0 || i < XN) {
+        if constexpr (XV)
+          *reinterpret_cast<floatx4 *>(&xs[buf][i]) = x[j];
+        else
+          xs[buf][i] = x[j][0];
+      }
     }
   };
 
@@ -313,7 +324,7 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
 
   const int nc = (K + CH - 1) / CH;
   float wa[RW][POS][VW], wb[RW][POS][VW];
-  float xr[XPT];
+  floatx4 xr[XPT];
   load_x(xr, 0);
   load_w(wa, 0);
   store_x(xr, 0);
@@ -360,7 +371,7 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
   }
 }
 
-template <bool VEC, int RW, int LPR, int CH_SHORT>
+template <bool VEC, int RW, int LPR, int CH_SHORT, bool XV>
 hipError_t launch_rows_rw(const GemmArgs &a, int transA, hipStream_t s) {
   constexpr int RPW = (64 / LPR) * RW;  // rows per wave
   const long long wgs = ((long long)a.N + kRowsWaves * RPW - 1) / (kRowsWaves * RPW);
@@ -371,7 +382,7 @@ hipError_t launch_rows_rw(const GemmArgs &a, int transA, hipStream_t s) {
 #define FP32GEMM_ROWS_CASE(MR)                                                                 \
   case MR:                                                                                     \
     hipLaunchKernelGGL((sgemv_rows_kernel<MR, VEC, RW, LPR,                                    \
-                                          LPR == 64 ? (MR <= 4 ? 1024 : 512) : CH_SHORT>),     \
+                                          LPR == 64 ? (MR <= 4 ? 1024 : 512) : CH_SHORT, XV>), \
                        grid, block, 0, s, a, transA);                                          \
     break;
     FP32GEMM_ROWS_CASE(1)
@@ -404,17 +415,27 @@ bool gemv_supported(const GemmArgs &a, int transA) {
 hipError_t launch_gemv_rows(const GemmArgs &a, int transA, int rows_per_wave, hipStream_t s) {
   if (!gemv_supported(a, transA)) return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.K % 4 == 0 && a.ldb % 4 == 0;
+  // X staged with float4 loads when op(A) = A has 16-byte aligned rows
+  const bool xv = vec && !transA && (uintptr_t)a.A % 16 == 0 && a.lda % 4 == 0;
   const int rw = rows_per_wave > 0 ? rows_per_wave : a.M >= 4 ? 2 : 1;
-  if (a.K < 1024 || (a.M >= 4 && a.K == 1024)) {
-    if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 16, 256>(a, transA, s)
-                            : launch_rows_rw<true, 1, 16, 256>(a, transA, s);
-    return rw >= 2 ? launch_rows_rw<false, 2, 16, 256>(a, transA, s)
-                   : launch_rows_rw<false, 1, 16, 256>(a, transA, s);
+  const bool short_rows = a.K < 1024 || (a.M >= 4 && a.K == 1024);
+  if (xv) {
+    if (short_rows)
+      return rw >= 2 ? launch_rows_rw<true, 2, 16, 256, true>(a, transA, s)
+                     : launch_rows_rw<true, 1, 16, 256, true>(a, transA, s);
+    return rw >= 2 ? launch_rows_rw<true, 2, 64, 0, true>(a, transA, s)
+                   : launch_rows_rw<true, 1, 64, 0, true>(a, transA, s);
   }
-  if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 64, 0>(a, transA, s)
-                          : launch_rows_rw<true, 1, 64, 0>(a, transA, s);
-  return rw >= 2 ? launch_rows_rw<false, 2, 64, 0>(a, transA, s)
-                 : launch_rows_rw<false, 1, 64, 0>(a, transA, s);
+  if (short_rows) {
+    if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 16, 256, false>(a, transA, s)
+                            : launch_rows_rw<true, 1, 16, 256, false>(a, transA, s);
+    return rw >= 2 ? launch_rows_rw<false, 2, 16, 256, false>(a, transA, s)
+                   : launch_rows_rw<false, 1, 16, 256, false>(a, transA, s);
+  }
+  if (vec) return rw >= 2 ? launch_rows_rw<true, 2, 64, 0, false>(a, transA, s)
+                          : launch_rows_rw<true, 1, 64, 0, false>(a, transA, s);
+  return rw >= 2 ? launch_rows_rw<false, 2, 64, 0, false>(a, transA, s)
+                 : launch_rows_rw<false, 1, 64, 0, false>(a, transA, s);
 }
 
 namespace {
