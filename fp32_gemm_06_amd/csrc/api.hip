@@ -82,6 +82,17 @@ int run_gemv(int cfg, int ta, const GemmArgs &a, hipStream_t s) {
   return (int)cfgs[cfg].launch(a, ta, s);
 }
 
+// The product on the kernel that suits it: M <= 8 on a GEMV kernel (row dots
+// when op(B) = B^T, column stripes otherwise; a.batch entries in one grid),
+// everything else (and op(A) = A^T with a very large lda) on the tiled kernel.
+int run_product(int ta, int tb, const GemmArgs &a, hipStream_t s) {
+  if (gemv_supported(a, ta)) {
+    if (tb) return (int)launch_gemv_rows(a, ta, -1, s);
+    return run_gemv(select_gemv_config_batched(a.M, a.N, a.K, a.batch), ta, a, s);
+  }
+  return run_gemm(-1, ta, tb, a, s);
+}
+
 GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
               int ldb, float beta, float *C, int ldc) {
   GemmArgs a;
@@ -109,8 +120,7 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (M <= 8) return run_gemv(-1, 0, a, s);
-  return run_gemm(-1, 0, 0, a, s);
+  return run_product(0, 0, a, s);
 }
 
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -131,9 +141,7 @@ int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const flo
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (gemv_supported(a, transA))
-    return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
-  return run_gemm(-1, transA, transB, a, s);
+  return run_product(transA, transB, a, s);
 }
 
 int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alpha,
@@ -150,10 +158,7 @@ int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alp
   if (batch_count > 65535) return -kPosBatched.batch;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (gemv_supported(a, transA))
-    return transB ? (int)launch_gemv_rows(a, transA, -1, s)
-                  : run_gemv(select_gemv_config_batched(M, N, K, batch_count), transA, a, s);
-  return run_gemm(-1, transA, transB, a, s);
+  return run_product(transA, transB, a, s);
 }
 
 int sgemm_fused(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
@@ -167,9 +172,7 @@ int sgemm_fused(int transA, int transB, int M, int N, int K, float alpha, const 
   a.act = act == FP32GEMM_ACT_RELU ? kActRelu : kActNone;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  if (gemv_supported(a, transA))
-    return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
-  return run_gemm(-1, transA, transB, a, s);
+  return run_product(transA, transB, a, s);
 }
 
 size_t sgemm_splitk_workspace_size(int M, int N, int K, int splits) {
@@ -196,11 +199,7 @@ int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha, const
   if (quick_return(a, s, &rc)) return rc;
   int kc = 0;
   const int chunks = M <= 8 ? 1 : splitk_chunk(K, splits > 0 ? splits : splitk_pick(M, N, K), &kc);
-  if (chunks <= 1) {  // one chunk: the plain routine (no workspace needed)
-    if (gemv_supported(a, transA))
-      return transB ? (int)launch_gemv_rows(a, transA, -1, s) : run_gemv(-1, transA, a, s);
-    return run_gemm(-1, transA, transB, a, s);
-  }
+  if (chunks <= 1) return run_product(transA, transB, a, s);  // the plain routine, no workspace
   if (workspace == nullptr) return -15;
   if (workspace_bytes < (size_t)chunks * (size_t)M * (size_t)N * sizeof(float)) return -16;
   // phase 1: chunk c of K as batch entry c, raw sums into workspace plane c
