@@ -202,7 +202,10 @@ def config_names(kind: int):
     return [fp32gemm_config_name(kind, i) for i in range(fp32gemm_num_configs(kind))]
 
 
-def _ld(t, name):
+def _layout(t, name, allow_transposed=True):
+    """(transposed, leading dimension) of a 2-D float32 GPU tensor that is
+    row-major (unit column stride) or, when allowed, a transposed view of a
+    row-major matrix (unit row stride)."""
     import torch
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
@@ -211,17 +214,24 @@ def _ld(t, name):
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
     r, c = t.shape
-    if c > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must have unit column stride (row-major)")
-    return t.stride(0) if r > 1 else max(1, c)
+    if c <= 1 or t.stride(1) == 1:
+        return 0, (t.stride(0) if r > 1 else max(1, c))
+    if allow_transposed and (r <= 1 or t.stride(0) == 1):
+        return 1, (t.stride(1) if c > 1 else max(1, r))
+    raise ValueError(f"{name} must be row-major or a transposed view of a row-major matrix")
 
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, config: int | None = None,
-         stream=None):
-    """Torch wrapper: returns C = alpha A @ B + beta C (C allocated when None).
+         stream=None, bias=None, act: int | str | None = None):
+    """Torch wrapper: returns C = act(alpha A @ B + beta C + bias) (C allocated
+    when None).
 
+    A and B may be row-major or transposed views of row-major matrices
+    (``W.t()`` of a stored N x K weight); C must be row-major.  ``bias`` (N
+    floats) and ``act`` ("relu" or ACT_RELU) select the fused epilogue.
     ``config`` forces a configuration of the SGEMM family (``sgemv`` family
-    when ``A`` has at most 8 rows and ``config`` is given as ("gemv", id)).
+    when ``A`` has at most 8 rows and ``config`` is given as ("gemv", id));
+    it needs row-major A and B and no epilogue.
     """
     import torch
     M, K = A.shape
@@ -234,14 +244,32 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, config: int | None
             raise ValueError("beta != 0 needs C")
     if tuple(C.shape) != (M, N):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
-    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
-    args = (M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc, stream)
-    if config is None:
-        rc = sgemm(*args)
-    elif isinstance(config, tuple) and config[0] == "gemv":
-        rc = fp32gemm_sgemv_with_config(config[1], *args)
+    ta, lda = _layout(A, "A")
+    tb, ldb = _layout(B, "B")
+    _, ldc = _layout(C, "C", allow_transposed=False)
+    if act in (None, "none"):
+        act = ACT_NONE
+    elif act == "relu":
+        act = ACT_RELU
+    if bias is not None:
+        if tuple(bias.shape) != (N,) or bias.dtype != torch.float32 or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous float32 vector of {N} values")
+    fused = bias is not None or act != ACT_NONE
+    if config is not None:
+        if ta or tb or fused:
+            raise ValueError("a forced configuration needs row-major A and B and no epilogue")
+        args = (M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc, stream)
+        if isinstance(config, tuple) and config[0] == "gemv":
+            rc = fp32gemm_sgemv_with_config(config[1], *args)
+        else:
+            rc = fp32gemm_sgemm_with_config(int(config), *args)
+    elif fused:
+        rc = sgemm_fused(ta, tb, M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc,
+                         bias, int(act), stream)
+    elif ta or tb:
+        rc = sgemm_ex(ta, tb, M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc, stream)
     else:
-        rc = fp32gemm_sgemm_with_config(int(config), *args)
+        rc = sgemm(M, N, K, float(alpha), A, lda, B, ldb, float(beta), C, ldc, stream)
     if rc != 0:
         raise Fp32GemmError(rc)
     return C

@@ -109,3 +109,32 @@ def test_deterministic_and_stream_independent():
             other = fg.gemm(dA, dB)
         s.synchronize()
         assert torch.equal(other, first)
+
+
+def test_gemm_wrapper_views_and_epilogue():
+    """gemm() maps transposed torch views onto sgemm_ex and bias/act onto
+    sgemm_fused; bit-exact on integer data."""
+    torch = require_gpu()
+    import fp32_gemm_06_amd as fg
+    M, N, K = 70, 90, 110
+    g = inputs.rng(77)
+    A = g.integers(-4, 5, size=(M, K)).astype(np.float32)
+    B = g.integers(-4, 5, size=(K, N)).astype(np.float32)
+    C0 = g.integers(-4, 5, size=(M, N)).astype(np.float32)
+    bias = g.integers(-9, 10, size=N).astype(np.float32)
+    dA = torch.from_numpy(A).cuda()
+    dAt = torch.from_numpy(np.ascontiguousarray(A.T)).cuda().t()     # a transposed view
+    dBt = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().t()     # W.t() of an N x K weight
+    want = oracle.sgemm(A, B, C0, 1.0, 0.5)
+    for a in (dA, dAt):
+        C = torch.from_numpy(C0).cuda()
+        fg.gemm(a, dBt, C, beta=0.5)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), want)
+    C = torch.from_numpy(C0).cuda()
+    fg.gemm(dAt, dBt, C, beta=0.5, bias=torch.from_numpy(bias).cuda(), act="relu")
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy().astype(np.float64),
+                          oracle.sgemm_fused(A, B, C0, 1.0, 0.5, bias, oracle.ACT_RELU))
+    with pytest.raises(ValueError):
+        fg.gemm(dA, dBt, config=0)
