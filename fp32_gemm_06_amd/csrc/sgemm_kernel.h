@@ -324,7 +324,10 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   // the last barrier freed (staged path: into registers, written to that
   // buffer just before the barrier).  Fragments are read one group of four
   // MFMA steps ahead; the last group's MFMAs run after the barrier, so they
-  // cover the first LDS reads of the next slice.
+  // cover the first LDS reads of the next slice.  A scheduling barrier keeps
+  // the other groups' MFMAs above the slice barrier: left to itself the
+  // compiler sinks most of them below it, which moves the wait for this
+  // wave's DMA earlier in the slice (measured 0.3% slower at 4096^3).
   constexpr int NGW = T::NGW;
   const int g0 = kg * NGW;  // this wave's first step group of a slice
   Frag f0, f1;
@@ -342,6 +345,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
         read_frag(cur, g0 + g + 1, fn);
         mma(fc);
       } else {
+        __builtin_amdgcn_sched_barrier(0);
         if (more) commit(nxt);
         if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
         __syncthreads();
@@ -391,6 +395,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
             read_frag(cur + STAGE, g0, fn);
             mma(fc);
           } else {
+            __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next stage of this wave landed
             __syncthreads();
             if (st + 1 < nst) read_frag(nbase, g0, fn);
