@@ -47,7 +47,7 @@ _SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_
 EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_fused", "sgemm_splitk",
            "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits", "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
-           "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
+           "fp32gemm_round_split", "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
 
 
 class Fp32GemmError(RuntimeError):
@@ -87,6 +87,8 @@ def lib():
         L.fp32gemm_config_name.restype = ctypes.c_char_p
         L.fp32gemm_select_config.argtypes = [ctypes.c_int] * 4
         L.fp32gemm_select_config.restype = ctypes.c_int
+        L.fp32gemm_round_split.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_int)]
+        L.fp32gemm_round_split.restype = ctypes.c_int
         L.fp32gemm_sgemm_with_config.argtypes = [ctypes.c_int] + _GEMM_ARGTYPES
         L.fp32gemm_sgemm_with_config.restype = ctypes.c_int
         L.fp32gemm_sgemv_with_config.argtypes = [ctypes.c_int] + _GEMM_ARGTYPES
@@ -196,6 +198,14 @@ def fp32gemm_config_name(kind: int, cfg: int):
 
 def fp32gemm_select_config(kind: int, M: int, N: int, K: int) -> int:
     return lib().fp32gemm_select_config(kind, M, N, K)
+
+
+def fp32gemm_round_split(M: int, N: int, K: int, batch: int = 1):
+    """(dim, first): how the tiled kernel splits this product into two launches
+    (0 = one launch, 1 = columns [0, first) then the rest, 2 = the same over rows)."""
+    first = ctypes.c_int(0)
+    dim = lib().fp32gemm_round_split(M, N, K, batch, ctypes.byref(first))
+    return dim, first.value
 
 
 def config_names(kind: int):

@@ -82,6 +82,34 @@ int run_gemv(int cfg, int ta, const GemmArgs &a, hipStream_t s) {
   return (int)cfgs[cfg].launch(a, ta, s);
 }
 
+// The tiled kernel with the configuration the dispatcher picks, as one launch
+// or as two over column or row ranges of C (plan_round_split).  The second
+// product starts at an offset of 256 k1 elements along N or M: B (op(B) = B
+// as given: columns; B^T: storage rows), A (op(A) = A: rows; A^T: storage
+// columns), C and the bias move with it, and the strides between batch
+// entries stay.
+int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
+  const RoundSplit sp = plan_round_split(a.M, a.N, a.K, a.batch);
+  if (sp.dim == 0) return run_gemm(-1, ta, tb, a, s);
+  const size_t f = (size_t)sp.first;
+  GemmArgs p = a, q = a;
+  if (sp.dim == 1) {
+    p.N = sp.first;
+    q.N = a.N - sp.first;
+    q.B = tb ? a.B + f * (size_t)a.ldb : a.B + f;
+    q.C = a.C + f;
+    if (a.bias) q.bias = a.bias + f;
+  } else {
+    p.M = sp.first;
+    q.M = a.M - sp.first;
+    q.A = ta ? a.A + f : a.A + f * (size_t)a.lda;
+    q.C = a.C + f * (size_t)a.ldc;
+  }
+  const int rc = run_gemm(sp.main_cfg, ta, tb, p, s);
+  if (rc) return rc;
+  return run_gemm(-1, ta, tb, q, s);
+}
+
 // The product on the kernel that suits it: M <= 8 on a GEMV kernel (row dots
 // when op(B) = B^T, column stripes otherwise; a.batch entries in one grid),
 // everything else (and op(A) = A^T with a very large lda) on the tiled kernel.
@@ -90,7 +118,7 @@ int run_product(int ta, int tb, const GemmArgs &a, hipStream_t s) {
     if (tb) return (int)launch_gemv_rows(a, ta, -1, s);
     return run_gemv(select_gemv_config_batched(a.M, a.N, a.K, a.batch), ta, a, s);
   }
-  return run_gemm(-1, ta, tb, a, s);
+  return run_tiled(ta, tb, a, s);
 }
 
 GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -261,6 +289,12 @@ int fp32gemm_select_config(int kind, int M, int N, int K) {
   return FP32GEMM_ERR_CONFIG;
 }
 
+int fp32gemm_round_split(int M, int N, int K, int batch, int *first) {
+  const RoundSplit sp = plan_round_split(M, N, K, batch);
+  if (first) *first = sp.dim ? sp.first : 0;
+  return sp.dim;
+}
+
 int fp32gemm_sgemm_with_config(int cfg, int M, int N, int K, float alpha, const float *A,
                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
                                fp32gemm_stream_t stream) {
@@ -270,7 +304,7 @@ int fp32gemm_sgemm_with_config(int cfg, int M, int N, int K, float alpha, const 
   if (rc) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quick_return(a, s, &rc)) return rc;
-  return run_gemm(cfg, 0, 0, a, s);
+  return cfg < 0 ? run_tiled(0, 0, a, s) : run_gemm(cfg, 0, 0, a, s);
 }
 
 int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha, const float *A,

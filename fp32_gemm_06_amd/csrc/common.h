@@ -132,6 +132,14 @@ int select_gemm_config(int M, int N, int K);
 // The fallback model alone, for a grid of `mult` products of M x N (split-K
 // chunks); *rate receives the modelled TFLOP/s.
 int model_gemm_config(int M, int N, int mult, double *rate);
+// A tiled product as two launches over ranges of C: columns (dim 1) or rows
+// (dim 2) [0, first) in whole rounds of 256x256 tiles with configuration
+// main_cfg, the rest as a second product with its own configuration.
+// dim 0: one launch.
+struct RoundSplit {
+  int dim, first, main_cfg;
+};
+RoundSplit plan_round_split(int M, int N, int K, int batch);
 int select_gemv_config(int M, int N, int K);
 // GEMV choice for `batch` products of M x N (the grid is stripes x batch).
 int select_gemv_config_batched(int M, int N, int K, int batch);

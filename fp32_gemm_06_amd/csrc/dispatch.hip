@@ -75,23 +75,26 @@ const char *gemm_config_name(int id) {
 // 64x64 tile gets a further factor for fewer than four workgroups per CU,
 // which stops falling at one per CU (256 tiles).  Checked against the sweep,
 // the estimate picks the measured best of the three tiles at 15 of the 16
-// swept shapes (at 2048^3 the two it confuses are 1.7% apart); tiny shapes
+// swept shapes (at 2048^3 the two it confuses are 0.3% apart); tiny shapes
 // such as 128^3 get the 64x64 tile.
+namespace {
+struct ModelTile {
+  const char *name;
+  int bm, bn;
+  double full_rate;  // TFLOP/s with every CU busy
+  bool small;        // 4-wave tile that needs several workgroups per CU
+};
+const ModelTile kModelTiles[] = {
+    {"256x256x32_w128x64_g4", 256, 256, 145.0, false},
+    {"128x128x32_w64x32_g4", 128, 128, 141.0, false},
+    {"64x64x32_w32x32_g4", 64, 64, 133.0, true},
+};
+}  // namespace
+
 int model_gemm_config(int M, int N, int mult, double *rate_out) {
-  struct Candidate {
-    const char *name;
-    int bm, bn;
-    double full_rate;  // TFLOP/s with every CU busy
-    bool small;        // 4-wave tile that needs several workgroups per CU
-  };
-  static const Candidate cands[] = {
-      {"256x256x32_w128x64_g4", 256, 256, 145.0, false},
-      {"128x128x32_w64x32_g4", 128, 128, 141.0, false},
-      {"64x64x32_w32x32_g4", 64, 64, 133.0, true},
-  };
   int best = -1;
   double best_rate = -1.0;
-  for (const Candidate &c : cands) {
+  for (const ModelTile &c : kModelTiles) {
     const double tiles = (double)((M + c.bm - 1) / c.bm) * (double)((N + c.bn - 1) / c.bn) * mult;
     const double rounds = (double)(long long)((tiles + 255.0) / 256.0);
     // each round costs a whole tile's work per CU; only M x N x mult of it is useful
@@ -107,19 +110,6 @@ int model_gemm_config(int M, int N, int mult, double *rate_out) {
   return best >= 0 ? best : 0;
 }
 
-// Fallback for shapes the table does not list.  The pages observe that a grid
-// with too few blocks leaves the GPU idle ("CUDA 矩阵乘法优化", section
-// "10. cuBLAS 领先的性能差异"), and that edge tiles waste the part of the
-// tile outside the matrix ("GPU 基础原理", section "最后一个考虑：分块的量化").
-// The estimate per tile shape is its full-load rate on MI355X (measured by
-// the sweep) scaled by the useful fraction of the work: each of the rounds
-// of up to 256 tiles (one 8-wave workgroup per CU at full rate) costs a whole
-// tile's work, of which M x N of the rounds' tile area is useful.  The 4-wave
-// 64x64 tile gets a further factor for fewer than four workgroups per CU,
-// which stops falling at one per CU (256 tiles).  Checked against the sweep,
-// the estimate picks the measured best of the three tiles at 15 of the 16
-// swept shapes (at 2048^3 the two it confuses are 1.7% apart); tiny shapes
-// such as 128^3 get the 64x64 tile.
 int select_gemm_config(int M, int N, int K) {
   for (const ShapeEntry &e : kGemmTable)
     if (e.M == M && e.N == N && e.K == K) {
@@ -127,6 +117,46 @@ int select_gemm_config(int M, int N, int K) {
       if (id >= 0) return id;
     }
   return model_gemm_config(M, N, 1, nullptr);
+}
+
+// Tile quantization across two launches.  When the 256x256 tiles of a
+// product overflow whole rounds of 256 (one per CU), the last round runs
+// partly empty, and the smaller tiles that fill the GPU better run at a lower
+// rate.  Splitting C instead into the columns (or rows) that fill exact rounds
+// of 256x256 tiles and the rest, run as a second product with its own tile,
+// keeps most of the work on the fast tile.  The model above prices both
+// launches, plus 3 us for the second one; the split is taken when it is
+// estimated at least 1% faster.  Measured (one box, 18 shapes the model
+// flags): never slower, and 2-4% faster where the rest or the single launch
+// falls to the 64x64 tile (2048 x 11008 x 4096: 1357 -> 1308 us).
+RoundSplit plan_round_split(int M, int N, int K, int batch) {
+  RoundSplit r{0, 0, -1};
+  const int big = find_gemm("256x256x32_w128x64_g8");
+  if (big < 0 || batch < 1 || M < 1 || N < 1 || K < 1) return r;
+  const double work = 2.0 * (double)K * (double)batch;  // flop per element of C
+  double rate = 0.0;
+  (void)model_gemm_config(M, N, batch, &rate);
+  double best = work * (double)M * (double)N / (rate * 1e6) * 0.99;  // us
+  const long long tm = (M + 255) / 256, tn = (N + 255) / 256;
+  for (int dim = 1; dim <= 2; ++dim) {
+    const long long across = dim == 1 ? tm : tn;  // tiles across the split
+    const long long along = dim == 1 ? tn : tm;   // tiles along the split dimension
+    long long k1 = along - 1;
+    while (k1 >= 1 && (across * k1 * batch) % 256 != 0) --k1;
+    if (k1 < 1) continue;
+    const int first = (int)(256 * k1);
+    const int m1 = dim == 1 ? M : first, n1 = dim == 1 ? first : N;
+    const int m2 = dim == 1 ? M : M - first, n2 = dim == 1 ? N - first : N;
+    double r1 = 0.0, r2 = 0.0;
+    (void)model_gemm_config(m1, n1, batch, &r1);
+    (void)model_gemm_config(m2, n2, batch, &r2);
+    const double t = work * ((double)m1 * n1 / (r1 * 1e6) + (double)m2 * n2 / (r2 * 1e6)) + 3.0;
+    if (t < best) {
+      best = t;
+      r = RoundSplit{dim, first, big};
+    }
+  }
+  return r;
 }
 
 int select_gemv_config(int M, int N, int K) { return select_gemv_config_batched(M, N, K, 1); }

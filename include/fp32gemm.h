@@ -199,6 +199,12 @@ const char *fp32gemm_config_name(int kind, int cfg);
 /* The configuration sgemm()/sgemv() would pick for this shape (kind as above). */
 int fp32gemm_select_config(int kind, int M, int N, int K);
 
+/* Whether the tiled kernel runs this product (batch entries of M x N x K) as
+ * two launches: 0 = one launch; 1 = columns [0, *first) of C in whole rounds
+ * of 256x256 tiles, then the remaining columns; 2 = the same over rows.
+ * *first (may be NULL) receives the split point, 0 for one launch. */
+int fp32gemm_round_split(int M, int N, int K, int batch, int *first);
+
 /*
  * sgemm / sgemv with a forced configuration (cfg = -1 picks as the plain
  * entry point does).  Same contract and codes as sgemm; the M <= 8 routing

@@ -212,3 +212,23 @@ def test_fused_argument_checks_need_no_gpu(lib):
     assert f(M=0, A=None, B=None, C=None, act=1) == 0
     # alpha == 0, beta == 1 and no epilogue: C is left alone without a launch
     assert f(alpha=0.0, beta=1.0, A=None, B=None) == 0
+
+
+def test_round_split_plan():
+    """The dispatcher's two-launch plan: one launch where the 256x256 tiles
+    fill whole rounds (or the split would not pay), and where it splits, the
+    first part is whole rounds of 256 tiles and the rest is non-empty."""
+    assert fg.fp32gemm_round_split(4092, 4092, 4092) == (0, 0)
+    assert fg.fp32gemm_round_split(4096, 4096, 4096) == (0, 0)
+    assert fg.fp32gemm_round_split(8192, 8192, 8192) == (0, 0)
+    assert fg.fp32gemm_round_split(128, 128, 128) == (0, 0)
+    assert fg.fp32gemm_round_split(2048, 11008, 4096) == (1, 8192)
+    assert fg.fp32gemm_round_split(3072, 8192, 4096) == (2, 2048)
+    for (M, N, K, b) in [(2048, 11008, 4096, 1), (3072, 8192, 4096, 1), (4096, 13824, 4096, 1),
+                         (8192, 32000, 4096, 1), (256, 300, 1024, 256), (1024, 28672, 4096, 1)]:
+        dim, first = fg.fp32gemm_round_split(M, N, K, b)
+        assert dim in (1, 2)
+        across = -(-M // 256) if dim == 1 else -(-N // 256)
+        along = N if dim == 1 else M
+        assert first % 256 == 0 and 0 < first < along
+        assert (across * (first // 256) * b) % 256 == 0
