@@ -9,6 +9,9 @@ calls the vendor library) on the same device buffers, alpha = 1, beta = 0,
 fp32 with TF32 disabled.
 
     python -m fp32_gemm_06_amd.sizesweep --out sweep.jsonl
+    python -m fp32_gemm_06_amd.sizesweep --out llm.jsonl --shapes 2048x11008x4096 ...
+
+`--shapes` takes M x N x K products (row-major, op = nn) instead of squares.
 """
 from __future__ import annotations
 
@@ -24,6 +27,8 @@ def main():
     ap.add_argument("--sizes", type=int, nargs="*", default=SIZES)
     ap.add_argument("--ops", nargs="*", default=["nn"], choices=["nn", "nt", "tn", "tt"],
                     help="operand layouts: n = as given, t = stored transposed")
+    ap.add_argument("--shapes", nargs="*", default=None,
+                    help="MxNxK products to time instead of the squares (nn only)")
     ap.add_argument("--md", default=None, help="also write a markdown table here")
     a = ap.parse_args()
 
@@ -53,6 +58,24 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
 
+    def describe(M, N, K):
+        """The configuration sgemm runs: one tile, or two launches (round split)."""
+        dim, first = fg.fp32gemm_round_split(M, N, K, 1)
+        if dim == 0:
+            return fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, M, N, K))
+        if dim == 1:
+            rest = fg.fp32gemm_select_config(0, M, N - first, K)
+            where = f"cols <{first}"
+        else:
+            rest = fg.fp32gemm_select_config(0, M - first, N, K)
+            where = f"rows <{first}"
+        return f"{where}: 256x256x32_w128x64_g8; rest: {fg.fp32gemm_config_name(0, rest)}"
+
+    if a.shapes:
+        cases = [tuple(int(v) for v in sh.lower().split("x")) + ("nn",) for sh in a.shapes]
+    else:
+        cases = [(n, n, n, op) for n in a.sizes for op in a.ops]
+
     # warm the clock before the first size
     big = torch.randn(4096, 4096, device=dev)
     for _ in range(60):
@@ -60,41 +83,43 @@ def main():
     del big
     recs = []
     with open(a.out, "w") as out:
-        for n in a.sizes:
-            for op in a.ops:
-                ta, tb = int(op[0] == "t"), int(op[1] == "t")
-                # storage: A is n x n either way; op(A) = A^T reads it transposed
-                A = torch.randn(n, n, device=dev)
-                B = torch.randn(n, n, device=dev)
-                C = torch.empty(n, n, device=dev)
-                opA = A.t() if ta else A
-                opB = B.t() if tb else B
+        for (M, N, K, op) in cases:
+            ta, tb = int(op[0] == "t"), int(op[1] == "t")
+            # storage: op(A) = A^T reads A stored K x M, op(B) = B^T reads B stored N x K
+            A = torch.randn(K, M, device=dev) if ta else torch.randn(M, K, device=dev)
+            B = torch.randn(N, K, device=dev) if tb else torch.randn(K, N, device=dev)
+            C = torch.empty(M, N, device=dev)
+            opA = A.t() if ta else A
+            opB = B.t() if tb else B
 
-                def ours():
-                    rc = fg.sgemm_ex(ta, tb, n, n, n, 1.0, A, n, B, n, 0.0, C, n, stream.cuda_stream)
-                    if rc:
-                        raise fg.Fp32GemmError(rc)
+            def ours():
+                rc = fg.sgemm_ex(ta, tb, M, N, K, 1.0, A, A.shape[1], B, B.shape[1], 0.0, C, N,
+                                 stream.cuda_stream)
+                if rc:
+                    raise fg.Fp32GemmError(rc)
 
-                us_ours = timed(ours)
-                us_vendor = timed(lambda: torch.matmul(opA, opB))
-                ref = torch.matmul(opA.double(), opB.double())
-                err = float(((C.double() - ref).abs() /
-                             (opA.abs().double() @ opB.abs().double())).max())
-                rec = {"n": n, "op": op, "us": round(us_ours, 3),
-                       "tflops": round(2 * n ** 3 / us_ours / 1e6, 3),
-                       "vendor_us": round(us_vendor, 3),
-                       "vendor_tflops": round(2 * n ** 3 / us_vendor / 1e6, 3),
-                       "ratio": round(us_vendor / us_ours, 3), "max_rel_err": err,
-                       "config": fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, n, n, n))}
-                print(json.dumps(rec), flush=True)
-                out.write(json.dumps(rec) + "\n")
-                recs.append(rec)
-                del A, B, C
+            us_ours = timed(ours)
+            us_vendor = timed(lambda: torch.matmul(opA, opB))
+            ref = torch.matmul(opA.double(), opB.double())
+            err = float(((C.double() - ref).abs() /
+                         (opA.abs().double() @ opB.abs().double())).max())
+            flop = 2.0 * M * N * K
+            rec = {"M": M, "N": N, "K": K, "op": op, "us": round(us_ours, 3),
+                   "tflops": round(flop / us_ours / 1e6, 3),
+                   "vendor_us": round(us_vendor, 3),
+                   "vendor_tflops": round(flop / us_vendor / 1e6, 3),
+                   "ratio": round(us_vendor / us_ours, 3), "max_rel_err": err,
+                   "config": describe(M, N, K)}
+            print(json.dumps(rec), flush=True)
+            out.write(json.dumps(rec) + "\n")
+            recs.append(rec)
+            del A, B, C, ref
     if a.md:
-        lines = ["| n | op | sgemm us | sgemm TFLOP/s | vendor TFLOP/s | vendor time / ours "
+        lines = ["| M x N x K | op | sgemm us | sgemm TFLOP/s | vendor TFLOP/s | vendor time / ours "
                  "| max_rel_err | config |", "|---" * 8 + "|"]
         for r in recs:
-            lines.append(f"| {r['n']} | {r['op']} | {r['us']} | {r['tflops']} | {r['vendor_tflops']} "
+            shape = f"{r['M']} x {r['N']} x {r['K']}"
+            lines.append(f"| {shape} | {r['op']} | {r['us']} | {r['tflops']} | {r['vendor_tflops']} "
                          f"| {r['ratio']} | {r['max_rel_err']:.1e} | {r['config']} |")
         with open(a.md, "w") as f:
             f.write("\n".join(lines) + "\n")

@@ -127,12 +127,21 @@ def sweep(out_path: str, reps: int, warm: int, only: str | None):
             torch.cuda.empty_cache()
 
 
-# SGEMM near-ties: tile-ordering groups of one tile shape often time within
-# the sweep's noise of each other, but a larger group shares more A and B
-# panels in each XCD's L2 (at 4092^3, group 8 fetched 407 MB per launch from
-# the fabric against 603 MB for group 2, for the same time).  Within this
-# fraction of the fastest time the largest group of the fastest tile wins.
+# SGEMM near-ties.  Tiles: the 4-wave 64x64 tile, four workgroups to a CU,
+# varies most from GPU to GPU (at 2048^3 it timed 0.3% ahead of 128x128 on
+# the sweep's GPU and 8% behind on another), so within TIE_TILE of the fastest
+# time the largest tile wins.  Groups: tile-ordering groups of one tile shape
+# often time within the sweep's noise of each other, but a larger group
+# shares more A and B panels in each XCD's L2 (at 4092^3, group 8 fetched
+# 407 MB per launch from the fabric against 603 MB for group 2), so within
+# TIE of that tile's fastest time the largest group wins.
+TIE_TILE = 0.01
 TIE = 0.005
+
+
+def _tile_area(config: str) -> int:
+    bm, bn = config.split("x")[:2]
+    return int(bm) * int(bn)
 
 
 def best_by_shape(path: str):
@@ -147,10 +156,13 @@ def best_by_shape(path: str):
     for k, rs in rows.items():
         b = min(rs, key=lambda r: r["us"])
         if k[0] == "gemm":
+            near = [r for r in rs if r["us"] <= b["us"] * (1 + TIE_TILE)]
+            area = max(_tile_area(r["config"]) for r in near)
+            b = min((r for r in near if _tile_area(r["config"]) == area), key=lambda r: r["us"])
             tile = b["config"].rsplit("_g", 1)[0]
-            near = [r for r in rs if r["config"].rsplit("_g", 1)[0] == tile
+            same = [r for r in rs if r["config"].rsplit("_g", 1)[0] == tile
                     and r["us"] <= b["us"] * (1 + TIE)]
-            b = max(near, key=lambda r: int(r["config"].rsplit("_g", 1)[1]))
+            b = max(same, key=lambda r: int(r["config"].rsplit("_g", 1)[1]))
         best[k] = b
     return best
 
