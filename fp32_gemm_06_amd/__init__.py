@@ -47,7 +47,8 @@ _SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_
 EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_fused", "sgemm_splitk",
            "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits", "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
-           "fp32gemm_round_split", "fp32gemm_sgemm_with_config", "fp32gemm_sgemv_with_config")
+           "fp32gemm_config_max_rows", "fp32gemm_round_split", "fp32gemm_sgemm_with_config",
+           "fp32gemm_sgemv_with_config")
 
 
 class Fp32GemmError(RuntimeError):
@@ -87,6 +88,8 @@ def lib():
         L.fp32gemm_config_name.restype = ctypes.c_char_p
         L.fp32gemm_select_config.argtypes = [ctypes.c_int] * 4
         L.fp32gemm_select_config.restype = ctypes.c_int
+        L.fp32gemm_config_max_rows.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.fp32gemm_config_max_rows.restype = ctypes.c_int
         L.fp32gemm_round_split.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_int)]
         L.fp32gemm_round_split.restype = ctypes.c_int
         L.fp32gemm_sgemm_with_config.argtypes = [ctypes.c_int] + _GEMM_ARGTYPES
@@ -198,6 +201,11 @@ def fp32gemm_config_name(kind: int, cfg: int):
 
 def fp32gemm_select_config(kind: int, M: int, N: int, K: int) -> int:
     return lib().fp32gemm_select_config(kind, M, N, K)
+
+
+def fp32gemm_config_max_rows(kind: int, cfg: int) -> int:
+    """The largest M a configuration runs (-1 for an unknown id)."""
+    return lib().fp32gemm_config_max_rows(kind, cfg)
 
 
 def fp32gemm_round_split(M: int, N: int, K: int, batch: int = 1):

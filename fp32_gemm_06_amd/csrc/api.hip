@@ -110,12 +110,30 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
   return run_gemm(-1, ta, tb, q, s);
 }
 
+// M = 9..128: the skinny MFMA kernel (N / 16 workgroups or more, each over
+// all of K), or the tiled kernel, whose 64x64 tiles number only
+// ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N, K =
+// 1024..32000 (8 weight copies, one box): the skinny kernel is faster for
+// every M <= 32 (4096^2, M = 16: 23.4 against 99.7 us), and above that
+// while the tiled kernel has fewer than 256 tiles (N = 11008, M = 64: 94.8
+// against 104.3 us; M = 96, 344 tiles: 193 against 134).
+bool skinny_pays(const GemmArgs &a) {
+  if (a.M <= 32) return true;
+  const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
+  return tiles < 256;
+}
+
 // The product on the kernel that suits it: M <= 8 on a GEMV kernel (row dots
 // when op(B) = B^T, column stripes otherwise; a.batch entries in one grid),
-// everything else (and op(A) = A^T with a very large lda) on the tiled kernel.
+// M = 9..128 on the skinny MFMA kernel where it pays, and everything else
+// (and op(A) = A^T with a very large lda) on the tiled kernel.
 int run_product(int ta, int tb, const GemmArgs &a, hipStream_t s) {
   if (gemv_supported(a, ta)) {
     if (tb) return (int)launch_gemv_rows(a, ta, -1, s);
+    return run_gemv(select_gemv_config_batched(a.M, a.N, a.K, a.batch), ta, a, s);
+  }
+  if (skinny_supported(a, ta) && skinny_pays(a)) {
+    if (tb) return (int)launch_skinny_tb(a, ta, s);
     return run_gemv(select_gemv_config_batched(a.M, a.N, a.K, a.batch), ta, a, s);
   }
   return run_tiled(ta, tb, a, s);
@@ -153,7 +171,7 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float
 
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, fp32gemm_stream_t stream) {
-  if (M < 1 || M > 8) return -1;
+  if (M < 1 || M > kSkinnyMaxRows) return -1;
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
   int rc = check_args(kPosSgemm, 0, 0, a);
   if (rc) return rc;
@@ -289,6 +307,16 @@ int fp32gemm_select_config(int kind, int M, int N, int K) {
   return FP32GEMM_ERR_CONFIG;
 }
 
+int fp32gemm_config_max_rows(int kind, int cfg) {
+  if (kind == 1) {
+    int n = 0;
+    const GemvConfig *c = gemv_configs(&n);
+    return (cfg >= 0 && cfg < n) ? c[cfg].max_rows : -1;
+  }
+  if (kind == 0) return (cfg >= 0 && cfg < num_gemm_config_ids()) ? 0x7fffffff : -1;
+  return -1;
+}
+
 int fp32gemm_round_split(int M, int N, int K, int batch, int *first) {
   const RoundSplit sp = plan_round_split(M, N, K, batch);
   if (first) *first = sp.dim ? sp.first : 0;
@@ -311,7 +339,11 @@ int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha, const 
                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
                                fp32gemm_stream_t stream) {
   if (cfg < -1 || cfg >= fp32gemm_num_configs(1)) return FP32GEMM_ERR_CONFIG;
-  if (M < 1 || M > 8) return -1;
+  if (M < 1 || M > kSkinnyMaxRows) return -1;
+  if (cfg >= 0) {
+    int n = 0;
+    if (!gemv_config_runs(gemv_configs(&n)[cfg], M)) return FP32GEMM_ERR_CONFIG;
+  }
   const GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
   int rc = check_args(kPosSgemm, 0, 0, a);
   if (rc) return rc;

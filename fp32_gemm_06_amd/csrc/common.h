@@ -90,18 +90,37 @@ void launchers_nt(GemmLaunchFn *out);
 void launchers_tn(GemmLaunchFn *out);
 void launchers_tt(GemmLaunchFn *out);
 
-// ---- GEMV (M <= 8) family -------------------------------------------------
+// ---- GEMV (M <= 32) family ------------------------------------------------
 struct GemvConfig {
   const char *name;
   int cbw;          // columns of W per workgroup
   int waves;        // waves per workgroup (they split K)
-  int unroll;       // rows of W per lane per pass
+  int unroll;       // rows of W per lane per pass (0: the MFMA kernel)
+  int max_rows;     // largest M the configuration runs
   hipError_t (*launch)(const GemmArgs &, int transA, hipStream_t);
 };
 const GemvConfig *gemv_configs(int *count);
 
 // The GEMV kernels take 1 <= M <= 8, and lda <= 2^17 when op(A) = A^T.
 bool gemv_supported(const GemmArgs &a, int transA);
+// The column-stripe kernel also takes 9 <= M <= kGemvMaxRows, on row
+// capacities 12, 16, 24 and 32 (gemv_row_capacity), in the configurations
+// for which gemv_config_runs says so.
+constexpr int kGemvMaxRows = 32;
+bool gemv_wide_supported(const GemmArgs &a, int transA);
+int gemv_row_capacity(int M);
+bool gemv_config_runs(const GemvConfig &c, int M);
+
+// Skinny MFMA kernel (skinny.hip), op(A) = A^T up to lda = 2^17; op(B) = B:
+// stripes of 16 columns of W for M <= 128, of 32 for M <= 64, of 64 for
+// M <= 32.
+constexpr int kSkinnyMaxRows = 128;
+bool skinny_supported(const GemmArgs &a, int transA);
+hipError_t launch_skinny16(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_skinny32(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_skinny64(const GemmArgs &a, int transA, hipStream_t s);
+// The same for op(B) = B^T (W stored N x K), 16 stored rows of W per workgroup.
+hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s);
 
 // Small-M product with op(B) = B^T (B stored N x K): row-dot kernel.
 // rows_per_wave is 1 or 2; <= 0 picks from M.

@@ -175,10 +175,22 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
   // workgroups.  The sweep over N from 1024 to 65536 is fastest with the
   // widest stripe that still leaves about 160 workgroups or more.
   (void)K;
+  if (M > 8) {
+    // The skinny MFMA kernel, with the same stripe-width rule as the GEMV:
+    // 64-column stripes (M <= 32) from N x batch = 10240, 32-column stripes
+    // (M <= 64) from 8192, else 16.  Measured: N = 11008, M = 16: 40.2 us
+    // on 64 columns against 69.5 on 16; N = K = 8192, M = 32: 65.3 on 32
+    // against 96.5 on 16; N = K = 4096: 16 columns best.
+    const char *mf = NB >= 160 * 64 && M <= 32   ? "mfma64_w8"
+                     : NB >= 256 * 32 && M <= 64 ? "mfma32_w8"
+                                                 : "mfma16_w8";
+    const int id = find_gemv(mf);
+    return id >= 0 ? id : 0;
+  }
   const char *name = NB >= 160 * 64   ? "c64_w8_u4"
                      : NB >= 256 * 32 ? "c32_w8_u4"
-                     : M >= 4        ? "c16_w4_u8"
-                                     : "c16_w8_u4";
+                     : M >= 4 && M <= 8 ? "c16_w4_u8"
+                                        : "c16_w8_u4";
   const int id = find_gemv(name);
   return id >= 0 ? id : 0;
 }

@@ -1,4 +1,4 @@
-// Small-M product Y[M x N] <- alpha X[M x K] W[K x N] + beta Y, 1 <= M <= 8.
+// Small-M product Y[M x N] <- alpha X[M x K] W[K x N] + beta Y, 1 <= M <= 32.
 //
 // This is the decode-phase shape of "GPU GEMM 优化完全拆解（一）", section
 // "LLM 推理本质上是 GEMM 的串联": M is the batch, and the time is the time to
@@ -29,7 +29,12 @@
 //    out-of-range buffer offset, so passes run in whole pairs;
 //  * partial sums are added across the lane groups of a wave with a fixed
 //    butterfly, then across waves in LDS in wave order: the summation order
-//    does not depend on timing, so results are bit-reproducible.
+//    does not depend on timing, so results are bit-reproducible;
+//  * M from 1 to 8 has a kernel per M; M from 9 to 32 (several decode
+//    sequences at once) runs on row capacities 12, 16, 24 and 32 with the
+//    rows past M masked: no X loads, no stores.  The multiply is then
+//    4 MR FMAs per 16 bytes of W, which the vector ALUs still keep up with
+//    at N = K = 4096 up to about M = 16.
 #include "common.h"
 
 namespace fp32gemm {
@@ -42,6 +47,7 @@ constexpr int kGemvMaxLdaT = 1 << 17;
 template <int MR, bool VEC, int CBW, int NW, int U>
 __global__ void __launch_bounds__(NW * 64)
 sgemv_kernel(GemmArgs a, int transA) {
+  constexpr bool CAP = MR > 8;        // a row capacity: rows m >= M are masked
   constexpr int VW = VEC ? 4 : 1;     // columns per lane
   constexpr int LPR = CBW / VW;       // lanes per row
   constexpr int RPI = 64 / LPR;       // rows per wave instruction
@@ -106,7 +112,7 @@ sgemv_kernel(GemmArgs a, int transA) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = tid + j * THREADS, m = i / ROWS, kk = i % ROWS;
-      const bool ok = i < XN && k0 + kk < K;
+      const bool ok = i < XN && k0 + kk < K && (!CAP || m < a.M);
       const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
       x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     }
@@ -179,7 +185,7 @@ sgemv_kernel(GemmArgs a, int transA) {
   const float alpha = a.alpha, beta = a.beta;
   for (int o = tid; o < MR * CBW; o += NW * 64) {
     const int m = o / CBW, c = o % CBW;
-    if (n0 + c >= a.N) continue;
+    if (n0 + c >= a.N || (CAP && m >= a.M)) continue;
     float s = red[0][m][c];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) s += red[w2][m][c];
@@ -405,6 +411,16 @@ bool gemv_supported(const GemmArgs &a, int transA) {
   return a.M >= 1 && a.M <= 8 && (!transA || a.lda <= kGemvMaxLdaT);
 }
 
+bool gemv_wide_supported(const GemmArgs &a, int transA) {
+  return a.M > 8 && a.M <= kGemvMaxRows && (!transA || a.lda <= kGemvMaxLdaT);
+}
+
+int gemv_row_capacity(int M) {
+  return M <= 8 ? M : M <= 12 ? 12 : M <= 16 ? 16 : M <= 24 ? 24 : M <= 32 ? 32 : 0;
+}
+
+bool gemv_config_runs(const GemvConfig &c, int M) { return M >= 1 && M <= c.max_rows; }
+
 // Rows per wave: one for M <= 3 (the most waves, which keeps the most loads
 // in flight), two from M = 4 on (each staged X value then feeds two rows).
 // Short rows share a wave instruction, 16 lanes (64 floats per instruction)
@@ -457,6 +473,11 @@ scale_kernel(float *C, int M, int N, int ldc, long long sC, float beta, const fl
   }
 }
 
+// Configurations that also run M = 9..32 (row capacities): four rows of W per
+// lane and at most 8 waves; the others spill their registers at 16+ rows.
+template <int NW, int U>
+constexpr bool kGemvWide = U == 4 && NW <= 8;
+
 template <bool VEC, int CBW, int NW, int U>
 hipError_t launch_cfg(const GemmArgs &a, int transA, hipStream_t s) {
   const long long blocks = ((long long)a.N + CBW - 1) / CBW;
@@ -474,8 +495,21 @@ hipError_t launch_cfg(const GemmArgs &a, int transA, hipStream_t s) {
     FP32GEMM_GEMV_CASE(6)
     FP32GEMM_GEMV_CASE(7)
     FP32GEMM_GEMV_CASE(8)
+    default:
+      if constexpr (kGemvWide<NW, U>) {
+        const int cap = gemv_row_capacity(a.M);
+        switch (cap) {
+          FP32GEMM_GEMV_CASE(12)
+          FP32GEMM_GEMV_CASE(16)
+          FP32GEMM_GEMV_CASE(24)
+          FP32GEMM_GEMV_CASE(32)
+          default: return hipErrorInvalidValue;
+        }
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
 #undef FP32GEMM_GEMV_CASE
-    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -483,7 +517,8 @@ hipError_t launch_cfg(const GemmArgs &a, int transA, hipStream_t s) {
 // 128-bit loads of W need B 16-byte aligned and N, ldb multiples of 4.
 template <int CBW, int NW, int U>
 hipError_t launch_gemv(const GemmArgs &a, int transA, hipStream_t s) {
-  if (!gemv_supported(a, transA)) return hipErrorInvalidValue;
+  if (!gemv_supported(a, transA) && !(kGemvWide<NW, U> && gemv_wide_supported(a, transA)))
+    return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
   return vec ? launch_cfg<true, CBW, NW, U>(a, transA, s) : launch_cfg<false, CBW, NW, U>(a, transA, s);
 }
@@ -492,14 +527,17 @@ hipError_t launch_gemv(const GemmArgs &a, int transA, hipStream_t s) {
 
 const GemvConfig *gemv_configs(int *count) {
   static const GemvConfig table[] = {
-      {"c16_w8_u8", 16, 8, 8, &launch_gemv<16, 8, 8>},
-      {"c16_w8_u4", 16, 8, 4, &launch_gemv<16, 8, 4>},
-      {"c16_w16_u4", 16, 16, 4, &launch_gemv<16, 16, 4>},
-      {"c16_w4_u8", 16, 4, 8, &launch_gemv<16, 4, 8>},
-      {"c16_w4_u16", 16, 4, 16, &launch_gemv<16, 4, 16>},
-      {"c32_w8_u4", 32, 8, 4, &launch_gemv<32, 8, 4>},
-      {"c32_w8_u8", 32, 8, 8, &launch_gemv<32, 8, 8>},
-      {"c64_w8_u4", 64, 8, 4, &launch_gemv<64, 8, 4>},
+      {"c16_w8_u8", 16, 8, 8, 8, &launch_gemv<16, 8, 8>},
+      {"c16_w8_u4", 16, 8, 4, kGemvMaxRows, &launch_gemv<16, 8, 4>},
+      {"c16_w16_u4", 16, 16, 4, 8, &launch_gemv<16, 16, 4>},
+      {"c16_w4_u8", 16, 4, 8, 8, &launch_gemv<16, 4, 8>},
+      {"c16_w4_u16", 16, 4, 16, 8, &launch_gemv<16, 4, 16>},
+      {"c32_w8_u4", 32, 8, 4, kGemvMaxRows, &launch_gemv<32, 8, 4>},
+      {"c32_w8_u8", 32, 8, 8, 8, &launch_gemv<32, 8, 8>},
+      {"c64_w8_u4", 64, 8, 4, kGemvMaxRows, &launch_gemv<64, 8, 4>},
+      {"mfma16_w8", 16, 8, 0, 128, &launch_skinny16},
+      {"mfma32_w8", 32, 8, 0, 64, &launch_skinny32},
+      {"mfma64_w8", 64, 8, 0, 32, &launch_skinny64},
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -1,0 +1,361 @@
+// Skinny product Y[M x N] <- alpha X[M x K] W[K x N] + beta Y for 9 <= M <= 128:
+// several decode sequences at once against a weight matrix.
+//
+// Like M <= 8 ("GPU GEMM 优化完全拆解（一）", section "LLM 推理本质上是 GEMM 的
+// 串联": the decode GEMMs stream W once from HBM), the time is set by the
+// weight read until M reaches about a hundred, but from M ~ 16 on the vector
+// ALUs of the column-stripe GEMV (4 M FMAs per 16 bytes of W) fall behind
+// that stream, and the tiled kernel has too few tiles (64 for M <= 64 at
+// N = 4096) to keep the memory system busy.  This kernel keeps the GEMV's
+// memory pattern and does the arithmetic on the matrix cores:
+//
+//  * a workgroup owns a 16-column stripe of W over the whole of K (N / 16
+//    workgroups, 256 at N = 4096; the two stripes of a 128-byte line run on
+//    one XCD), and its 8 waves split each pass of ROWS rows of K;
+//  * W values go straight from buffer loads into the B operand of
+//    v_mfma_f32_16x16x4_f32 (lane l holds B[k = l / 16][n = l % 16]).  The
+//    sum over a pass is the same under any assignment of its k to (step,
+//    lane quarter); step g of lane quarter q takes k = 16 (g / 4) + 4 q +
+//    g % 4 of the wave's part of the pass, so four consecutive steps of a
+//    lane are four consecutive k and the four quarters cover 16 consecutive k;
+//  * W stored K x N: a wave instruction reads four 64-byte row segments;
+//    stored N x K (TB): lane (q, c) reads stored row n0 + c along k, and a
+//    wave instruction reads 64 contiguous bytes of each of 16 rows;
+//  * X is staged per pass in LDS as [m][k] rows (stride ROWS + 4 floats, so
+//    the eight 16-byte reads an LDS cycle serves fall in distinct banks); one
+//    ds_read_b128 holds the A operand of four consecutive steps;
+//  * M up to 16 MB rows, MB blocks of 16 sharing each W value; passes run two
+//    deep (W in two register sets, X in two LDS buffers), with the same
+//    branch-free masking as the GEMV: rows of X past M and rows of W past K
+//    read zeros through an out-of-range buffer offset;
+//  * the waves' partial sums are added in LDS in wave order: the result does
+//    not depend on timing.
+#include "common.h"
+
+namespace fp32gemm {
+namespace {
+
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = kSkWaves * 64;
+
+template <int E> struct Vec { typedef float type __attribute__((ext_vector_type(E))); };
+template <> struct Vec<1> { typedef float type; };
+
+// One raw buffer load of E floats (E = 1, 2, 4) at voffset + soffset bytes.
+template <int E>
+__device__ __forceinline__ typename Vec<E>::type load_vec(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                         int soff) {
+  if constexpr (E == 4)
+    return __builtin_bit_cast(typename Vec<4>::type,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+  else if constexpr (E == 2)
+    return __builtin_bit_cast(typename Vec<2>::type,
+                              __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+  else
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+}
+
+template <int E>
+__device__ __forceinline__ float elem(const typename Vec<E>::type &v, int e) {
+  if constexpr (E == 1)
+    return v;
+  else
+    return v[e];
+}
+
+// MB: blocks of 16 rows of X (M <= 16 MB).  NB: column blocks of 16 per
+// workgroup; lane (q, c) loads NB consecutive columns n0 + NB c .. + NB - 1
+// of a row of W, and column block e of the MFMA takes element e, so its
+// column c stands for n0 + NB c + e.  TA: op(A) = A^T (X stored K x M).
+// XV: float4 loads of X (op(A) = A, 16-byte aligned rows, K % 4 == 0).
+// TB: op(B) = B^T (W stored N x K, a linear layer's weight): lane (q, c)
+// reads stored row n0 + c along k, WV floats at a time (4 when the rows are
+// 16-byte aligned and K % 4 == 0), each float one MFMA step; NB = 1.
+template <int MB, int NB, bool TA, bool XV, bool TB = false, int WV = 1>
+__global__ void __launch_bounds__(kSkThreads)
+skinny_kernel(GemmArgs a) {
+  constexpr int MR = 16 * MB;               // row capacity of X
+  constexpr int CW = 16 * NB;               // columns of W per workgroup
+  constexpr int ROWS = 1024 / (MB * NB);    // rows of K per pass
+  constexpr int RW = ROWS / kSkWaves;       // rows per wave per pass
+  constexpr int G = RW / 4;                 // MFMA steps per wave per pass (rows per lane quarter)
+  constexpr int SK = ROWS + 4;              // LDS row stride of the X chunk, in floats
+  // accumulator sets: with few independent blocks, consecutive steps
+  // alternate between sets so that no MFMA waits on the one before it
+  constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
+  constexpr int XBUF = 2 * MR * SK, RED = kSkWaves * MR * CW;
+  static_assert(G % 4 == 0, "A fragments are read four steps at a time");
+  static_assert(!TB || (NB == 1 && G % WV == 0), "stored-transposed W: one column block");
+  static_assert((XBUF > RED ? XBUF : RED) * 4 <= 160 * 1024, "fits in LDS");
+  __shared__ __attribute__((aligned(16))) float xs[XBUF > RED ? XBUF : RED];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, c = lane & 15;
+
+  // (batch entry, stripe) from the linear workgroup id; with 16-column
+  // stripes the two of a 128-byte line run on one XCD (id % 8)
+  const int GX = gridDim.x;
+  const long long L = (long long)blockIdx.y * GX + blockIdx.x;
+  const long long T = (long long)gridDim.y * GX;
+  const long long w = L < (T & ~15LL) ? 2 * (8 * ((L >> 3) >> 1) + (L & 7)) + ((L >> 3) & 1) : L;
+  const long long bz = w / GX;
+  const int cb = (int)(w - bz * GX);
+  a.A += bz * a.sA;
+  a.B += bz * a.sB;
+  a.C += bz * a.sC;
+  const int n0 = cb * CW;
+  // NB > 1: N % NB == 0, so a lane's NB columns are all inside N or all past it
+  const bool col_ok = n0 + (TB ? c : NB * c) < a.N;
+  const int K = a.K;
+
+  // W at k = 16 (g / 4) + 4 q + g % 4 of the wave's part of the pass (the
+  // wave's first row is the buffer base): 4 q in the per-lane offset, the
+  // rest in the scalar offset.  Stored transposed: stored row n0 + c, WV
+  // consecutive k per load.
+  typedef typename Vec<NB>::type wvec_t;
+  constexpr int WL = TB ? G / WV : G;  // W loads per wave per pass
+  typedef typename Vec<TB ? WV : NB>::type wload_t;
+  auto kstep = [](int g) { return 16 * (g / 4) + g % 4; };  // k of step g, lane quarter 0
+  const uint32_t w_lane =
+      TB ? ((uint32_t)c * (uint32_t)a.ldb + (uint32_t)(4 * q)) * 4u
+         : ((uint32_t)(4 * q) * (uint32_t)a.ldb + (uint32_t)(NB * c)) * 4u;
+  auto load_w = [&](wload_t (&wv)[WL], int k0) {
+    const int r0 = k0 + wave * RW;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(TB ? a.B + (size_t)n0 * a.ldb + r0 : a.B + (size_t)r0 * a.ldb + n0);
+#pragma unroll
+    for (int g = 0; g < WL; ++g) {
+      // load g covers steps g WV .. g WV + WV - 1 (TB) or step g
+      const int kk = kstep(TB ? g * WV : g);
+      // WV == 4: K % 4 == 0 and kk + 4 q is a multiple of 4, so the four k
+      // are all inside K or all past it
+      const bool ok = col_ok && r0 + 4 * q + kk < K;
+      wv[g] = load_vec<TB ? WV : NB>(rw, ok ? w_lane : kOob, (TB ? kk : kk * a.ldb) * 4);
+    }
+  };
+  // the B operand of step g, column block e
+  auto b_of = [&](const wload_t (&wv)[WL], int g, int e) -> float {
+    if constexpr (TB)
+      return elem<WV>(wv[g / WV], g % WV);
+    else
+      return elem<NB>(wv[g], e);
+  };
+
+  // X of the pass at k0: MR rows of ROWS values, consecutive threads along k
+  // (X stored M x K) or along m (stored K x M) so the reads are coalesced.
+  // Load j of a thread covers element (m_l + m_j, k_l + k_j): a per-lane part
+  // and a part that is the same for every lane.
+  static_assert(!(TA && XV), "float4 X loads only for op(A) = A");
+  constexpr int XE = XV ? 4 : 1;                     // floats per load
+  constexpr int P = kSkThreads * XE;                 // floats per load round
+  constexpr int XP = MR * ROWS / P;                  // loads per thread
+  static_assert(MR * ROWS % P == 0, "X loads divide evenly");
+  typedef typename Vec<XE>::type xvec_t;
+  int m_l, k_l;
+  if constexpr (TA) {
+    m_l = tid % MR;
+    k_l = tid / MR;
+  } else if constexpr (P % ROWS == 0) {
+    m_l = tid * XE / ROWS;
+    k_l = tid * XE % ROWS;
+  } else {
+    m_l = 0;
+    k_l = tid * XE;
+  }
+  auto x_part = [&](int j, int &m_j, int &k_j) {
+    if constexpr (TA) {
+      m_j = 0;
+      k_j = j * (kSkThreads / MR);
+    } else if constexpr (P % ROWS == 0) {
+      m_j = j * (P / ROWS);
+      k_j = 0;
+    } else {
+      m_j = j / (ROWS / P);
+      k_j = (j % (ROWS / P)) * P;
+    }
+  };
+  const uint32_t x_lane =
+      (TA ? (uint32_t)k_l * (uint32_t)a.lda + (uint32_t)m_l : (uint32_t)m_l * (uint32_t)a.lda + (uint32_t)k_l) * 4u;
+  auto load_x = [&](xvec_t (&xv)[XP], int k0) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(TA ? a.A + (size_t)k0 * a.lda : a.A + k0);
+#pragma unroll
+    for (int j = 0; j < XP; ++j) {
+      int m_j, k_j;
+      x_part(j, m_j, k_j);
+      // XV: K % 4 == 0, so a float4 is all inside K or all past it
+      const bool ok = m_l + m_j < a.M && k0 + k_l + k_j < K;
+      const int so = (TA ? k_j * a.lda + m_j : m_j * a.lda + k_j) * 4;
+      xv[j] = load_vec<XE>(rx, ok ? x_lane : kOob, so);
+    }
+  };
+  auto store_x = [&](const xvec_t (&xv)[XP], int buf) {
+    float *base = &xs[buf * MR * SK + m_l * SK + k_l];
+#pragma unroll
+    for (int j = 0; j < XP; ++j) {
+      int m_j, k_j;
+      x_part(j, m_j, k_j);
+      *reinterpret_cast<xvec_t *>(base + m_j * SK + k_j) = xv[j];
+    }
+  };
+
+  floatx4 acc[NA][MB][NB];
+#pragma unroll
+  for (int s = 0; s < NA; ++s)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int e = 0; e < NB; ++e) acc[s][j][e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // step g = 4 t + s of this lane: A = X[16 j + c][wave RW + 16 t + 4 q + s],
+  // B = element e of the W value of step g
+  auto compute = [&](const wload_t (&wv)[WL], int buf) {
+    const float *xb = &xs[buf * MR * SK + c * SK + wave * RW + 4 * q];
+#pragma unroll
+    for (int t = 0; t < G / 4; ++t) {
+      floatx4 av[MB];
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        av[j] = *reinterpret_cast<const floatx4 *>(xb + 16 * j * SK + 16 * t);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < NB; ++e)
+#pragma unroll
+          for (int j = 0; j < MB; ++j) {
+            floatx4 &d = acc[(4 * t + s) % NA][j][e];
+            d = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][s], b_of(wv, 4 * t + s, e), d, 0, 0, 0);
+          }
+    }
+  };
+
+  wload_t wa[WL], wb[WL];
+  xvec_t xr[XP];
+  load_x(xr, 0);
+  load_w(wa, 0);
+  store_x(xr, 0);
+  __syncthreads();
+  // the scheduling barriers keep each prefetch ahead of the compute that
+  // waits on the previous pass
+  for (int k0 = 0; k0 < K; k0 += 2 * ROWS) {
+    load_x(xr, k0 + ROWS);
+    load_w(wb, k0 + ROWS);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wa, 0);
+    store_x(xr, 1);
+    __syncthreads();
+    load_x(xr, k0 + 2 * ROWS);
+    load_w(wa, k0 + 2 * ROWS);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wb, 1);
+    store_x(xr, 0);
+    __syncthreads();
+  }
+
+  // Partial sums: accumulator sets in order, then the waves in wave order
+  // through LDS (the X buffers are free: the loop ended on a barrier).
+  // Output layout of v_mfma_f32_16x16x4_f32: lane (q, c), element r holds
+  // D[4 q + r][c]; column c of block e is column NB c + e of the stripe.
+  float *red = xs;  // [wave][MR][CW]
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      floatx4 v = acc[0][j][e];
+#pragma unroll
+      for (int s = 1; s < NA; ++s) v += acc[s][j][e];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(wave * MR + 16 * j + 4 * q + r) * CW + NB * c + e] = v[r];
+    }
+  __syncthreads();
+  const float alpha = a.alpha, beta = a.beta;
+  for (int o = tid; o < MR * CW; o += kSkThreads) {
+    const int m = o / CW, cc = o % CW;
+    if (m >= a.M || n0 + cc >= a.N) continue;
+    float s = red[o];
+#pragma unroll
+    for (int w2 = 1; w2 < kSkWaves; ++w2) s += red[w2 * MR * CW + o];
+    float *y = a.C + (size_t)m * a.ldc + n0 + cc;
+    float out = alpha * s;
+    if (beta != 0.0f) out += beta * *y;
+    if (a.bias) out += a.bias[n0 + cc];
+    *y = apply_act(out, a.act);
+  }
+}
+
+template <int MB, int NB, bool TB = false, int WV = 1>
+hipError_t launch_mb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
+  const long long blocks = ((long long)a.N + 16 * NB - 1) / (16 * NB);
+  if (blocks > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks, (unsigned)a.batch), block(kSkThreads);
+  if (transA)
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, true, false, TB, WV>), grid, block, 0, s, a);
+  else if (xv)
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, false, true, TB, WV>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, false, false, TB, WV>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// W stored N x K: float4 loads along k when its rows are 16-byte aligned.
+template <int MB>
+hipError_t launch_mb_tb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
+  const bool wv4 = (uintptr_t)a.B % 16 == 0 && a.ldb % 4 == 0 && a.K % 4 == 0 &&
+                   (a.batch == 1 || a.sB % 4 == 0);
+  return wv4 ? launch_mb<MB, 1, true, 4>(a, transA, xv, s)
+             : launch_mb<MB, 1, true, 1>(a, transA, xv, s);
+}
+
+// NB column blocks of 16 per workgroup; M <= 16 MB with MB * NB <= 8.
+template <int NB>
+hipError_t launch_nb(const GemmArgs &a, int transA, hipStream_t s) {
+  if (a.M < 1 || a.M > 128 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
+  // NB > 1: W rows read NB floats at a time (B 4 NB-byte aligned, N and ldb
+  // multiples of NB); otherwise the 16-column kernel runs
+  if (NB > 1 && ((uintptr_t)a.B % (4 * NB) != 0 || a.N % NB != 0 || a.ldb % NB != 0 ||
+                 (a.batch > 1 && a.sB % NB != 0)))
+    return launch_nb<1>(a, transA, s);
+  // float4 loads of X need 16-byte aligned rows and whole float4s inside K
+  const bool xv = !transA && (uintptr_t)a.A % 16 == 0 && a.lda % 4 == 0 && a.K % 4 == 0 &&
+                  (a.batch == 1 || a.sA % 4 == 0);
+  if (a.M <= 16) return launch_mb<1, NB>(a, transA, xv, s);
+  if constexpr (NB <= 4) {
+    if (a.M <= 32) return launch_mb<2, NB>(a, transA, xv, s);
+  }
+  if constexpr (NB <= 2) {
+    if (a.M <= 64) return launch_mb<4, NB>(a, transA, xv, s);
+  }
+  if constexpr (NB == 1) return launch_mb<8, NB>(a, transA, xv, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool skinny_supported(const GemmArgs &a, int transA) {
+  // op(A) = A^T: the offsets of a pass (ROWS <= 1024 rows of lda floats)
+  // stay within 31 bits up to lda = 2^17
+  return a.M >= 1 && a.M <= kSkinnyMaxRows && (!transA || a.lda <= (1 << 17));
+}
+
+hipError_t launch_skinny16(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_nb<1>(a, transA, s);
+}
+
+hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s) {
+  if (!skinny_supported(a, transA)) return hipErrorInvalidValue;
+  const bool xv = !transA && (uintptr_t)a.A % 16 == 0 && a.lda % 4 == 0 && a.K % 4 == 0 &&
+                  (a.batch == 1 || a.sA % 4 == 0);
+  if (a.M <= 16) return launch_mb_tb<1>(a, transA, xv, s);
+  if (a.M <= 32) return launch_mb_tb<2>(a, transA, xv, s);
+  if (a.M <= 64) return launch_mb_tb<4>(a, transA, xv, s);
+  return launch_mb_tb<8>(a, transA, xv, s);
+}
+hipError_t launch_skinny32(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_nb<2>(a, transA, s);
+}
+hipError_t launch_skinny64(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_nb<4>(a, transA, s);
+}
+
+}  // namespace fp32gemm

@@ -59,21 +59,26 @@ typedef struct ihipStream_t *fp32gemm_stream_t;
  * C[M x N] <- alpha * A[M x K] . B[K x N] + beta * C.
  * Argument checks: M, N, K >= 0; lda >= max(1, K); ldb >= max(1, N);
  * ldc >= max(1, N); A and B non-NULL when alpha != 0 and K > 0; C non-NULL
- * when M > 0 and N > 0.  M <= 8 is routed to the GEMV kernel (sgemv); larger
- * M runs the LDS-tiled fp32 MFMA kernel with the tile configuration that the
- * per-shape table selects for (M, N, K).
+ * when M > 0 and N > 0.  M <= 8 is routed to the GEMV kernel (sgemv), and
+ * M = 9..128 to the skinny MFMA kernel where it is the faster (M <= 32
+ * always, above that while the tiled kernel has fewer than 256 64x64 tiles);
+ * larger M runs the LDS-tiled fp32 MFMA kernel with the tile configuration
+ * that the per-shape table selects for (M, N, K).
  */
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
           fp32gemm_stream_t stream);
 
 /*
- * The same operation for 1 <= M <= 8 (the decode shape: X = A is M x K, the
- * weight W = B is K x N, Y = C is M x N).  Bandwidth-bound: each workgroup
- * streams a narrow block of W's columns over all of K with 128-bit loads,
- * its waves split K, and the partial sums are added inside the workgroup in
- * a fixed order (deterministic, no workspace, no atomics).  Returns -1 when
- * M is outside 1..8.
+ * The same operation for 1 <= M <= 128 (the decode shape: X = A is M x K, the
+ * weight W = B is K x N, Y = C is M x N; M is the number of sequences
+ * decoded at once).  Bandwidth-bound: each workgroup streams a narrow block
+ * of W's columns over all of K, its waves split K, and the partial sums are
+ * added inside the workgroup in a fixed order (deterministic, no workspace,
+ * no atomics).  Up to M = 32 the multiply can run on the vector ALUs
+ * (128-bit loads of W), up to M = 128 on the matrix cores (16-column
+ * stripes, v_mfma_f32_16x16x4_f32); the library picks by shape.  Returns -1
+ * when M is outside 1..128.
  */
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
@@ -199,6 +204,10 @@ const char *fp32gemm_config_name(int kind, int cfg);
 /* The configuration sgemm()/sgemv() would pick for this shape (kind as above). */
 int fp32gemm_select_config(int kind, int M, int N, int K);
 
+/* The largest M a configuration runs (kind as above; -1 for an unknown id):
+ * 8, 32 or 128 for the GEMV family, INT_MAX for the tiled family. */
+int fp32gemm_config_max_rows(int kind, int cfg);
+
 /* Whether the tiled kernel runs this product (batch entries of M x N x K) as
  * two launches: 0 = one launch; 1 = columns [0, *first) of C in whole rounds
  * of 256x256 tiles, then the remaining columns; 2 = the same over rows.
@@ -209,7 +218,9 @@ int fp32gemm_round_split(int M, int N, int K, int batch, int *first);
  * sgemm / sgemv with a forced configuration (cfg = -1 picks as the plain
  * entry point does).  Same contract and codes as sgemm; the M <= 8 routing
  * is not applied: fp32gemm_sgemm_with_config always runs the MFMA kernel and
- * fp32gemm_sgemv_with_config always the GEMV kernel (M must be 1..8).
+ * fp32gemm_sgemv_with_config always the GEMV family (M must be 1..128, and at
+ * most fp32gemm_config_max_rows of the configuration, else
+ * FP32GEMM_ERR_CONFIG).
  */
 int fp32gemm_sgemm_with_config(int cfg, int M, int N, int K, float alpha,
                                const float *A, int lda, const float *B,

@@ -121,9 +121,28 @@ def test_batched_argument_checks(lib):
 
 
 def test_gemv_batch_range(lib):
-    assert call(fg.sgemv, M=9) == -1
+    """M from 1 to 128; each configuration runs up to its own row limit."""
+    assert call(fg.sgemv, M=129) == -1
     assert call(fg.sgemv, M=0) == -1
-    assert fg.fp32gemm_sgemv_with_config(0, 9, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, 0) == -1
+    assert fg.fp32gemm_sgemv_with_config(0, 129, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, 0) == -1
+    names = fg.config_names(fg.KIND_SGEMV)
+    rows = [fg.fp32gemm_config_max_rows(fg.KIND_SGEMV, c) for c in range(len(names))]
+    assert set(rows) == {8, 32, 64, 128}
+    for cfg, name in enumerate(names):
+        # the 4-rows-per-lane, <= 8-wave GEMV configurations take 32 rows,
+        # the MFMA ones 32, 64 or 128 by stripe width, the others 8
+        if name.startswith("mfma"):
+            assert rows[cfg] == {"16": 128, "32": 64, "64": 32}[name[4:6]], name
+        else:
+            waves, unroll = (int(v[1:]) for v in name.split("_")[1:3])
+            assert rows[cfg] == (32 if unroll == 4 and waves <= 8 else 8), name
+        # M = 9 with a NULL C: a runnable configuration reaches the argument
+        # check (-10), the others stop at the configuration check
+        for M in (9, 33, 65):
+            rc = fg.fp32gemm_sgemv_with_config(cfg, M, 4, 4, 1.0, 16, 4, 16, 4, 0.0, None, 4, 0)
+            assert rc == (-10 if M <= rows[cfg] else fg.ERR_CONFIG), (name, M, rc)
+    assert fg.fp32gemm_config_max_rows(fg.KIND_SGEMV, len(names)) == -1
+    assert fg.fp32gemm_config_max_rows(fg.KIND_SGEMM, 0) > 128
 
 
 def test_configs(lib):

@@ -88,7 +88,7 @@ def test_argument_errors():
     for args, code in cases:
         assert fg.sgemm(*args) == code, (args, code)
         assert "invalid argument" in fg.strerror(code)
-    assert fg.sgemv(9, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4) == -1
+    assert fg.sgemv(129, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4) == -1
     assert fg.sgemv(0, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4) == -1
     assert fg.fp32gemm_sgemm_with_config(10 ** 6, 4, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4) == -100
     assert fg.fp32gemm_sgemv_with_config(10 ** 6, 4, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4) == -100

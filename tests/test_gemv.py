@@ -1,5 +1,8 @@
-"""The small-M (decode) kernel: every batch size 1..8, both load paths, every
-configuration, ragged N and K, padded leading dimensions."""
+"""The small-M (decode) kernels: every batch size 1..8, both load paths, every
+configuration, ragged N and K, padded leading dimensions; M = 9..128 on every
+configuration that takes it (vector-ALU row capacities up to 32, the skinny
+MFMA kernel up to 128), routed through sgemm, with op(A) = A^T, with the weight
+stored transposed and in strided batches."""
 import numpy as np
 import pytest
 
@@ -72,3 +75,85 @@ def test_transposed_x_huge_lda_falls_back(tb):
     (got,), ok = run_batched(1, tb, As, Bs, Cs, 1.0, 0.5, pads=(140000 - M, 0, 0))
     assert ok
     assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"huge lda tb={tb}")
+
+
+WIDE_M = [9, 12, 13, 16, 17, 24, 25, 32, 33, 48, 64, 65, 100, 128]
+
+
+@pytest.mark.parametrize("M", WIDE_M)
+def test_wide_rows_every_config(M):
+    """M = 9..128: every configuration of the GEMV family that runs this M
+    (vector-ALU stripes on row capacities up to 32, the skinny MFMA kernel on
+    16/32/64-column stripes up to 128/64/32 rows; rows past M masked), both
+    load paths, bit-exact, nothing written outside C; the configurations
+    whose row limit is below M are refused."""
+    require_gpu()
+    names = fg.config_names(fg.KIND_SGEMV)
+    rows = [fg.fp32gemm_config_max_rows(fg.KIND_SGEMV, c) for c in range(len(names))]
+    assert any(r >= M for r in rows)
+    for (N, K) in [(1000, 777), (333, 4099), (16, 5000)]:
+        A, B, C0 = inputs.random_case(M * 37 + N, M, N, K, kind="int")
+        ref = oracle.sgemm(A, B, C0, 1.0, 0.5)
+        for cfg in range(len(names)):
+            if rows[cfg] < M:
+                with pytest.raises(fg.Fp32GemmError):
+                    run_hip(A, B, C0, 1.0, 0.5, config=cfg, family="gemv")
+                continue
+            got, canary = run_hip(A, B, C0, 1.0, 0.5, config=cfg, family="gemv", guard=32)
+            assert canary, f"write outside C (M={M} N={N} {names[cfg]})"
+            assert_bitexact(got, ref, f"M={M} N={N} K={K} {names[cfg]}")
+
+
+@pytest.mark.parametrize("M", [9, 16, 24, 32, 48, 64, 96, 128])
+def test_wide_rows_routed(M):
+    """sgemm with M = 9..128 (the skinny kernel where it pays, the tiled
+    kernel where it has 256 tiles or more), and sgemv, against the oracle."""
+    require_gpu()
+    for (N, K) in [(4096, 1024), (24576, 256)]:
+        A, B, C0 = inputs.random_case(M + N, M, N, K, kind="uniform")
+        ref = oracle.sgemm(A, B, C0, 0.75, -1.0)
+        bnd = oracle.bound(A, B, C0, 0.75, -1.0)
+        for family in ("auto", "gemv"):
+            got, canary = run_hip(A, B, C0, 0.75, -1.0, family=family, guard=16)
+            assert canary
+            assert_parity(got, ref, bnd, f"M={M} N={N} K={K} {family}")
+
+
+@pytest.mark.parametrize("M", [10, 20, 32, 100])
+def test_wide_rows_transposed_x(M):
+    """op(A) = A^T with M = 9..128: the skinny kernel reads X with swapped strides."""
+    from test_transpose_batched import _case, run_batched
+    N, K = 530, 3001
+    As, Bs, Cs = _case(7200 + M, M, N, K)
+    (got,), ok = run_batched(1, 0, As, Bs, Cs, 1.0, 0.5, pads=(5, 4, 3), offset=1)
+    assert ok, "write outside C"
+    assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"M={M} op(A)=A^T")
+
+
+@pytest.mark.parametrize("ta", (0, 1))
+@pytest.mark.parametrize("M", [9, 16, 33, 64, 100, 128])
+def test_wide_rows_weight_transposed(ta, M):
+    """op(B) = B^T (weight stored N x K) with M = 9..128: the skinny kernel's
+    stored-row path, with 16-byte loads along k (aligned, K % 4 == 0) and
+    with 4-byte loads (K odd, and operands off 16-byte alignment)."""
+    from test_transpose_batched import _case, run_batched
+    for (N, K, offset) in [(530, 3000, 0), (530, 3001, 0), (47, 1024, 1)]:
+        As, Bs, Cs = _case(7400 + M + K, M, N, K)
+        (got,), ok = run_batched(ta, 1, As, Bs, Cs, 1.0, 0.5, pads=(3, 4, 5), offset=offset)
+        assert ok, "write outside C"
+        assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5),
+                        f"M={M} N={N} K={K} ta={ta} op(B)=B^T")
+
+
+def test_wide_rows_batched():
+    """Strided batches of M = 16, 27 and 70 entries in one skinny grid, both
+    weight layouts."""
+    from test_transpose_batched import _case, run_batched
+    for M in (16, 27, 70):
+        for tb in (0, 1):
+            As, Bs, Cs = _case(7300 + M, M, 200, 300, batch=3)
+            outs, ok = run_batched(0, tb, As, Bs, Cs, 1.0, 1.0, pads=(1, 2, 3), gaps=(7, 5, 3))
+            assert ok, "write outside C"
+            for b in range(3):
+                assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 1.0),
+                                f"M={M} tb={tb} entry {b}")

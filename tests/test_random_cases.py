@@ -2,8 +2,8 @@
 
 Each case draws an entry point (sgemm, sgemv, sgemm_ex, sgemm_strided_batched,
 sgemm_fused, sgemm_splitk, or sgemm / sgemv with a tile or GEMV configuration
-forced, drawn from all of them), a shape with M from the decode range (1..8) or
-up to a few tiles with ragged tails, operand transposes, padded leading
+forced, drawn from all of them), a shape with M from the decode range (1..8, or
+9..128 for the GEMV entry points) or up to a few tiles with ragged tails, operand transposes, padded leading
 dimensions, operands shifted off 16-byte alignment, alpha and beta (zero
 included), and for the fused and split-K entry points a bias, an activation and
 a chunk count.  The operands live in one device buffer each, padding columns
@@ -31,8 +31,12 @@ SENTINEL = 12345.0
 def draw_case(i):
     g = np.random.default_rng(9000 + i)
     entry = ENTRIES[i % len(ENTRIES)]
-    small = entry in ("sgemv", "sgemv_cfg") or g.random() < 0.3
-    M = int(g.integers(1, 9)) if small else int(g.integers(9, 331))
+    if entry in ("sgemv", "sgemv_cfg"):
+        M = int(g.integers(1, 9)) if g.random() < 0.5 else int(g.integers(9, 129))
+    elif g.random() < 0.3:
+        M = int(g.integers(1, 9))
+    else:
+        M = int(g.integers(9, 331))
     N = int(g.integers(1, 331))
     K = int(g.integers(1, 401))
     trans = entry in ("sgemm_ex", "batched", "fused", "splitk")
@@ -51,7 +55,10 @@ def draw_case(i):
     if entry == "sgemm_cfg":
         cfg = int(g.integers(0, fg.fp32gemm_num_configs(fg.KIND_SGEMM)))
     elif entry == "sgemv_cfg":
-        cfg = int(g.integers(0, fg.fp32gemm_num_configs(fg.KIND_SGEMV)))
+        # a configuration whose row limit takes this M
+        ok = [c for c in range(fg.fp32gemm_num_configs(fg.KIND_SGEMV))
+              if fg.fp32gemm_config_max_rows(fg.KIND_SGEMV, c) >= M]
+        cfg = ok[int(g.integers(0, len(ok)))]
     return dict(entry=entry, M=M, N=N, K=K, ta=ta, tb=tb, pads=pads, offset=offset,
                 alpha=alpha, beta=beta, kind=kind, batch=batch, has_bias=has_bias, act=act,
                 splits=splits, cfg=cfg, seed=9000 + i)
