@@ -19,8 +19,9 @@
 //    g % 4 of the wave's part of the pass, so four consecutive steps of a
 //    lane are four consecutive k and the four quarters cover 16 consecutive k;
 //  * W stored K x N: a wave instruction reads four 64-byte row segments;
-//    stored N x K (TB): lane (q, c) reads stored row n0 + c along k, and a
-//    wave instruction reads 64 contiguous bytes of each of 16 rows;
+//    stored N x K (TB): lane (q, c) reads stored rows n0 + 16 e + c along k
+//    (column block e), and a wave instruction reads 64 contiguous bytes of
+//    each of 16 consecutive rows;
 //  * X is staged per pass in LDS as [m][k] rows (stride ROWS + 4 floats, so
 //    the eight 16-byte reads an LDS cycle serves fall in distinct banks); one
 //    ds_read_b128 holds the A operand of four consecutive steps;
@@ -69,8 +70,9 @@ __device__ __forceinline__ float elem(const typename Vec<E>::type &v, int e) {
 // column c stands for n0 + NB c + e.  TA: op(A) = A^T (X stored K x M).
 // XV: float4 loads of X (op(A) = A, 16-byte aligned rows, K % 4 == 0).
 // TB: op(B) = B^T (W stored N x K, a linear layer's weight): lane (q, c)
-// reads stored row n0 + c along k, WV floats at a time (4 when the rows are
-// 16-byte aligned and K % 4 == 0), each float one MFMA step; NB = 1.
+// reads stored rows n0 + 16 e + c along k, WV floats at a time (4 when the
+// rows are 16-byte aligned and K % 4 == 0), each float one MFMA step; column
+// c of block e is then stripe column 16 e + c.
 template <int MB, int NB, bool TA, bool XV, bool TB = false, int WV = 1>
 __global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a) {
@@ -85,7 +87,7 @@ skinny_kernel(GemmArgs a) {
   constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
   constexpr int XBUF = 2 * MR * SK, RED = kSkWaves * MR * CW;
   static_assert(G % 4 == 0, "A fragments are read four steps at a time");
-  static_assert(!TB || (NB == 1 && G % WV == 0), "stored-transposed W: one column block");
+  static_assert(!TB || G % WV == 0, "stored-transposed W: whole vectors per pass");
   static_assert((XBUF > RED ? XBUF : RED) * 4 <= 160 * 1024, "fits in LDS");
   __shared__ __attribute__((aligned(16))) float xs[XBUF > RED ? XBUF : RED];
 
@@ -106,38 +108,54 @@ skinny_kernel(GemmArgs a) {
   a.C += bz * a.sC;
   const int n0 = cb * CW;
   // NB > 1: N % NB == 0, so a lane's NB columns are all inside N or all past it
-  const bool col_ok = n0 + (TB ? c : NB * c) < a.N;
+  const bool col_ok = n0 + NB * c < a.N;  // K x N layout
   const int K = a.K;
 
   // W at k = 16 (g / 4) + 4 q + g % 4 of the wave's part of the pass (the
   // wave's first row is the buffer base): 4 q in the per-lane offset, the
   // rest in the scalar offset.  Stored transposed: stored row n0 + c, WV
   // consecutive k per load.
-  typedef typename Vec<NB>::type wvec_t;
-  constexpr int WL = TB ? G / WV : G;  // W loads per wave per pass
+  constexpr int WL = TB ? G / WV * NB : G;  // W loads per wave per pass
   typedef typename Vec<TB ? WV : NB>::type wload_t;
+  // stripe column of element (block e, lane column c) of the MFMA output
+  auto col_of = [](int e, int cc) { return TB ? 16 * e + cc : NB * cc + e; };
   auto kstep = [](int g) { return 16 * (g / 4) + g % 4; };  // k of step g, lane quarter 0
-  const uint32_t w_lane =
-      TB ? ((uint32_t)c * (uint32_t)a.ldb + (uint32_t)(4 * q)) * 4u
-         : ((uint32_t)(4 * q) * (uint32_t)a.ldb + (uint32_t)(NB * c)) * 4u;
+  // Per-lane offsets.  The masks combine their conditions with "&": a
+  // short-circuit "col_ok && k < K" let LLVM branch around duplicated loads,
+  // each branch with a vmcnt(0) wait.  Stored N x K, the offset of column
+  // block e is already kOob for stored rows past N (measured faster there);
+  // stored K x N, the column test stays in each load's mask (folding it into
+  // the offset cost 11% at N = 11008, M = 32).
+  const uint32_t w_off = TB ? ((uint32_t)c * (uint32_t)a.ldb + (uint32_t)(4 * q)) * 4u
+                            : ((uint32_t)(4 * q) * (uint32_t)a.ldb + (uint32_t)(NB * c)) * 4u;
+  uint32_t w_lane[NB];
+#pragma unroll
+  for (int e = 0; e < NB; ++e) w_lane[e] = n0 + 16 * e + c < a.N ? w_off : kOob;
   auto load_w = [&](wload_t (&wv)[WL], int k0) {
     const int r0 = k0 + wave * RW;
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(TB ? a.B + (size_t)n0 * a.ldb + r0 : a.B + (size_t)r0 * a.ldb + n0);
 #pragma unroll
-    for (int g = 0; g < WL; ++g) {
-      // load g covers steps g WV .. g WV + WV - 1 (TB) or step g
-      const int kk = kstep(TB ? g * WV : g);
-      // WV == 4: K % 4 == 0 and kk + 4 q is a multiple of 4, so the four k
-      // are all inside K or all past it
-      const bool ok = col_ok && r0 + 4 * q + kk < K;
-      wv[g] = load_vec<TB ? WV : NB>(rw, ok ? w_lane : kOob, (TB ? kk : kk * a.ldb) * 4);
+    for (int l = 0; l < WL; ++l) {
+      if constexpr (TB) {
+        // load l: column block e = l / (WL / NB), steps (l % (WL / NB)) WV ..
+        // + WV - 1, so a row's chunks are requested back to back.
+        // WV == 4: K % 4 == 0 and kk + 4 q is a multiple of 4, so the four k
+        // are all inside K or all past it
+        const int e = l / (WL / NB), kk = kstep(l % (WL / NB) * WV);
+        wv[l] = load_vec<WV>(rw, r0 + 4 * q + kk < K ? w_lane[e] : kOob,
+                             (16 * e * a.ldb + kk) * 4);
+      } else {
+        // load l: step l, the lane's NB columns
+        const int kk = kstep(l);
+        wv[l] = load_vec<NB>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob, kk * a.ldb * 4);
+      }
     }
   };
   // the B operand of step g, column block e
   auto b_of = [&](const wload_t (&wv)[WL], int g, int e) -> float {
     if constexpr (TB)
-      return elem<WV>(wv[g / WV], g % WV);
+      return elem<WV>(wv[e * (WL / NB) + g / WV], g % WV);
     else
       return elem<NB>(wv[g], e);
   };
@@ -184,7 +202,7 @@ skinny_kernel(GemmArgs a) {
       int m_j, k_j;
       x_part(j, m_j, k_j);
       // XV: K % 4 == 0, so a float4 is all inside K or all past it
-      const bool ok = m_l + m_j < a.M && k0 + k_l + k_j < K;
+      const bool ok = (m_l + m_j < a.M) & (k0 + k_l + k_j < K);  // no short circuit
       const int so = (TA ? k_j * a.lda + m_j : m_j * a.lda + k_j) * 4;
       xv[j] = load_vec<XE>(rx, ok ? x_lane : kOob, so);
     }
@@ -229,33 +247,47 @@ skinny_kernel(GemmArgs a) {
     }
   };
 
-  wload_t wa[WL], wb[WL];
+  // W runs D passes deep (D register sets), X one pass ahead through the two
+  // LDS buffers.  A pass is ROWS rows, fewer as MB grows; stored N x K, the
+  // W loads of a pass are few (16-byte, WV = 4), and deeper sets keep more
+  // bytes in flight (4096^2, M = 128: 63.9 -> 58.0 us).  Stored K x N a pass
+  // has 4 NB times as many W loads, and vmcnt retires loads in issue order,
+  // so the wait for a pass's staged X also waits for every older W load:
+  // deeper sets only added waits there (M = 48: 41 -> 53 us), so it stays
+  // at two.  A wave keeps at most 63 loads in flight, which bounds D.
+  constexpr int D = !TB || MB == 1 ? 2 : MB <= 4 ? 4 : 8;
+  static_assert(D % 2 == 0, "pass parity selects the X buffer");
+  wload_t wr[D][WL];
   xvec_t xr[XP];
   load_x(xr, 0);
-  load_w(wa, 0);
+#pragma unroll
+  for (int p = 0; p + 1 < D; ++p) load_w(wr[p], p * ROWS);
   store_x(xr, 0);
   __syncthreads();
-  // the scheduling barriers keep each prefetch ahead of the compute that
-  // waits on the previous pass
-  for (int k0 = 0; k0 < K; k0 += 2 * ROWS) {
-    load_x(xr, k0 + ROWS);
-    load_w(wb, k0 + ROWS);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(wa, 0);
-    store_x(xr, 1);
-    __syncthreads();
-    load_x(xr, k0 + 2 * ROWS);
-    load_w(wa, k0 + 2 * ROWS);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(wb, 1);
-    store_x(xr, 0);
-    __syncthreads();
+  // The scheduling barriers keep each prefetch ahead of the compute that
+  // waits on an earlier pass.  Passes run in groups of D; a pass that starts
+  // past K (only in the last group) skips its multiply, its loads read zeros.
+  for (int k0 = 0; k0 < K; k0 += D * ROWS) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kp = k0 + u * ROWS;
+      load_x(xr, kp + ROWS);
+      load_w(wr[(u + D - 1) % D], kp + (D - 1) * ROWS);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (D > 2) {
+        if (kp < K) compute(wr[u], u % 2);
+      } else {
+        compute(wr[u], u % 2);  // at most one pass past K, on zeros
+      }
+      store_x(xr, (u + 1) % 2);
+      __syncthreads();
+    }
   }
 
   // Partial sums: accumulator sets in order, then the waves in wave order
   // through LDS (the X buffers are free: the loop ended on a barrier).
   // Output layout of v_mfma_f32_16x16x4_f32: lane (q, c), element r holds
-  // D[4 q + r][c]; column c of block e is column NB c + e of the stripe.
+  // D[4 q + r][c]; column c of block e is stripe column col_of(e, c).
   float *red = xs;  // [wave][MR][CW]
 #pragma unroll
   for (int j = 0; j < MB; ++j)
@@ -266,7 +298,7 @@ skinny_kernel(GemmArgs a) {
       for (int s = 1; s < NA; ++s) v += acc[s][j][e];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        red[(wave * MR + 16 * j + 4 * q + r) * CW + NB * c + e] = v[r];
+        red[(wave * MR + 16 * j + 4 * q + r) * CW + col_of(e, c)] = v[r];
     }
   __syncthreads();
   const float alpha = a.alpha, beta = a.beta;
@@ -299,12 +331,12 @@ hipError_t launch_mb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
 }
 
 // W stored N x K: float4 loads along k when its rows are 16-byte aligned.
-template <int MB>
+template <int MB, int NB>
 hipError_t launch_mb_tb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
   const bool wv4 = (uintptr_t)a.B % 16 == 0 && a.ldb % 4 == 0 && a.K % 4 == 0 &&
                    (a.batch == 1 || a.sB % 4 == 0);
-  return wv4 ? launch_mb<MB, 1, true, 4>(a, transA, xv, s)
-             : launch_mb<MB, 1, true, 1>(a, transA, xv, s);
+  return wv4 ? launch_mb<MB, NB, true, 4>(a, transA, xv, s)
+             : launch_mb<MB, NB, true, 1>(a, transA, xv, s);
 }
 
 // NB column blocks of 16 per workgroup; M <= 16 MB with MB * NB <= 8.
@@ -342,14 +374,31 @@ hipError_t launch_skinny16(const GemmArgs &a, int transA, hipStream_t s) {
   return launch_nb<1>(a, transA, s);
 }
 
-hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s) {
-  if (!skinny_supported(a, transA)) return hipErrorInvalidValue;
+// W stored N x K, 16 NB stored rows per workgroup (M <= 16 MB, MB NB <= 8).
+template <int NB>
+hipError_t launch_tb_nb(const GemmArgs &a, int transA, hipStream_t s) {
+  if (a.M < 1 || a.M > 128 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
   const bool xv = !transA && (uintptr_t)a.A % 16 == 0 && a.lda % 4 == 0 && a.K % 4 == 0 &&
                   (a.batch == 1 || a.sA % 4 == 0);
-  if (a.M <= 16) return launch_mb_tb<1>(a, transA, xv, s);
-  if (a.M <= 32) return launch_mb_tb<2>(a, transA, xv, s);
-  if (a.M <= 64) return launch_mb_tb<4>(a, transA, xv, s);
-  return launch_mb_tb<8>(a, transA, xv, s);
+  if (a.M <= 16) return launch_mb_tb<1, NB>(a, transA, xv, s);
+  if constexpr (NB <= 4) {
+    if (a.M <= 32) return launch_mb_tb<2, NB>(a, transA, xv, s);
+  }
+  if constexpr (NB <= 2) {
+    if (a.M <= 64) return launch_mb_tb<4, NB>(a, transA, xv, s);
+  }
+  if constexpr (NB == 1) return launch_mb_tb<8, NB>(a, transA, xv, s);
+  return hipErrorInvalidValue;
+}
+
+// Stripe width as for W stored K x N: 64 rows per workgroup (M <= 32) from
+// N x batch = 10240, 32 (M <= 64) from 8192, else 16.
+hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s) {
+  if (!skinny_supported(a, transA)) return hipErrorInvalidValue;
+  const long long nb = (long long)a.N * a.batch;
+  if (nb >= 160 * 64 && a.M <= 32) return launch_tb_nb<4>(a, transA, s);
+  if (nb >= 256 * 32 && a.M <= 64) return launch_tb_nb<2>(a, transA, s);
+  return launch_tb_nb<1>(a, transA, s);
 }
 hipError_t launch_skinny32(const GemmArgs &a, int transA, hipStream_t s) {
   return launch_nb<2>(a, transA, s);
