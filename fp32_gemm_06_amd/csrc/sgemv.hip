@@ -94,7 +94,7 @@ sgemv_kernel(GemmArgs a, int transA) {
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)(k0 + wrow) * a.ldb + n0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = col_ok && k0 + rl + u < K;
+      const bool ok = col_ok & (k0 + rl + u < K);  // "&": no short circuit, no branch
       const uint32_t off = ok ? (uint32_t)((g * U + u) * a.ldb + cl) * 4u : kOob;
       if constexpr (VEC) {
         const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
@@ -112,7 +112,7 @@ sgemv_kernel(GemmArgs a, int transA) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = tid + j * THREADS, m = i / ROWS, kk = i % ROWS;
-      const bool ok = i < XN && k0 + kk < K && (!CAP || m < a.M);
+      const bool ok = (i < XN) & (k0 + kk < K) & (!CAP | (m < a.M));
       const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
       x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     }
@@ -261,7 +261,7 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
 #pragma unroll
       for (int p = 0; p < POS; ++p) {
         const int k = k0 + p * STEP + li * VW;
-        const uint32_t off = live[r] && k < K ? rowoff[r] + (uint32_t)k * 4u : kOob;
+        const uint32_t off = (live[r] & (k < K)) ? rowoff[r] + (uint32_t)k * 4u : kOob;
         if constexpr (VEC) {
           const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 #pragma unroll
@@ -280,7 +280,7 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = XW * (tid + j * kRowsThreads), m = i / CH, kk = i % CH;
-      const bool ok = (XN % (XW * kRowsThreads) == 0 || i < XN) && k0 + kk < K;
+      const bool ok = ((XN % (XW * kRowsThreads) == 0) | (i < XN)) & (k0 + kk < K);
       const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
       if constexpr (XV)
         x[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
