@@ -248,14 +248,14 @@ skinny_kernel(GemmArgs a) {
   };
 
   // W runs D passes deep (D register sets), X one pass ahead through the two
-  // LDS buffers.  A pass is ROWS rows, fewer as MB grows; stored N x K, the
-  // W loads of a pass are few (16-byte, WV = 4), and deeper sets keep more
-  // bytes in flight (4096^2, M = 128: 63.9 -> 58.0 us).  Stored K x N a pass
-  // has 4 NB times as many W loads, and vmcnt retires loads in issue order,
-  // so the wait for a pass's staged X also waits for every older W load:
-  // deeper sets only added waits there (M = 48: 41 -> 53 us), so it stays
-  // at two.  A wave keeps at most 63 loads in flight, which bounds D.
-  constexpr int D = !TB || MB == 1 ? 2 : MB <= 4 ? 4 : 8;
+  // LDS buffers.  A pass is ROWS rows, fewer as MB grows, and deeper sets
+  // keep more bytes in flight: 4096^2, M = 128 went 63.9 -> 58.0 us (stored
+  // N x K) and 63.8 -> 59.6 (stored K x N).  vmcnt retires loads in issue
+  // order, so the wait for a pass's staged X also waits for every older W
+  // load; stored K x N with MB = 2 a pass has 4 NB times as many W loads as
+  // stored N x K, and depth 4 there only added waits (M = 32: 24.8 -> 27.0
+  // us).  A wave keeps at most 63 loads in flight, which bounds D.
+  constexpr int D = MB == 1 || (MB == 2 && !TB) ? 2 : MB <= 4 ? 4 : 8;
   static_assert(D % 2 == 0, "pass parity selects the X buffer");
   wload_t wr[D][WL];
   xvec_t xr[XP];
