@@ -9,9 +9,10 @@
 // N = 4096) to keep the memory system busy.  This kernel keeps the GEMV's
 // memory pattern and does the arithmetic on the matrix cores:
 //
-//  * a workgroup owns a 16-column stripe of W over the whole of K (N / 16
-//    workgroups, 256 at N = 4096; the two stripes of a 128-byte line run on
-//    one XCD), and its 8 waves split each pass of ROWS rows of K;
+//  * a workgroup owns a stripe of 16 NB columns of W (NB = 1, 2, 4; the
+//    library picks the widest stripe that still leaves enough workgroups)
+//    over the whole of K, and its 8 waves split each pass of ROWS rows of K;
+//    with 16-column stripes the two of a 128-byte line run on one XCD;
 //  * W values go straight from buffer loads into the B operand of
 //    v_mfma_f32_16x16x4_f32 (lane l holds B[k = l / 16][n = l % 16]).  The
 //    sum over a pass is the same under any assignment of its k to (step,
@@ -25,10 +26,10 @@
 //  * X is staged per pass in LDS as [m][k] rows (stride ROWS + 4 floats, so
 //    the eight 16-byte reads an LDS cycle serves fall in distinct banks); one
 //    ds_read_b128 holds the A operand of four consecutive steps;
-//  * M up to 16 MB rows, MB blocks of 16 sharing each W value; passes run two
-//    deep (W in two register sets, X in two LDS buffers), with the same
-//    branch-free masking as the GEMV: rows of X past M and rows of W past K
-//    read zeros through an out-of-range buffer offset;
+//  * M up to 16 MB rows, MB blocks of 16 sharing each W value; W runs D
+//    passes deep in registers and X one pass ahead through two LDS buffers,
+//    with the same branch-free masking as the GEMV: rows of X past M and
+//    rows of W past K (or N) read zeros through an out-of-range buffer offset;
 //  * the waves' partial sums are added in LDS in wave order: the result does
 //    not depend on timing.
 #include "common.h"
@@ -113,8 +114,8 @@ skinny_kernel(GemmArgs a) {
 
   // W at k = 16 (g / 4) + 4 q + g % 4 of the wave's part of the pass (the
   // wave's first row is the buffer base): 4 q in the per-lane offset, the
-  // rest in the scalar offset.  Stored transposed: stored row n0 + c, WV
-  // consecutive k per load.
+  // rest in the scalar offset.  Stored transposed: stored row n0 + 16 e + c
+  // for column block e, WV consecutive k per load.
   constexpr int WL = TB ? G / WV * NB : G;  // W loads per wave per pass
   typedef typename Vec<TB ? WV : NB>::type wload_t;
   // stripe column of element (block e, lane column c) of the MFMA output
@@ -148,7 +149,8 @@ skinny_kernel(GemmArgs a) {
       } else {
         // load l: step l, the lane's NB columns
         const int kk = kstep(l);
-        wv[l] = load_vec<NB>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob, kk * a.ldb * 4);
+        wv[l] = load_vec<NB>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob,
+                             kk * a.ldb * 4);
       }
     }
   };
@@ -193,8 +195,8 @@ skinny_kernel(GemmArgs a) {
       k_j = (j % (ROWS / P)) * P;
     }
   };
-  const uint32_t x_lane =
-      (TA ? (uint32_t)k_l * (uint32_t)a.lda + (uint32_t)m_l : (uint32_t)m_l * (uint32_t)a.lda + (uint32_t)k_l) * 4u;
+  const uint32_t x_lane = (TA ? (uint32_t)k_l * (uint32_t)a.lda + (uint32_t)m_l
+                               : (uint32_t)m_l * (uint32_t)a.lda + (uint32_t)k_l) * 4u;
   auto load_x = [&](xvec_t (&xv)[XP], int k0) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(TA ? a.A + (size_t)k0 * a.lda : a.A + k0);
 #pragma unroll
