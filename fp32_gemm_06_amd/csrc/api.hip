@@ -68,7 +68,7 @@ int quick_return(const GemmArgs &a, hipStream_t s, int *rc) {
 int run_gemm(int cfg, int ta, int tb, const GemmArgs &a, hipStream_t s) {
   int ntiles = 0;
   const GemmConfig *tiles = gemm_configs(&ntiles);
-  if (cfg < 0) cfg = select_gemm_config(a.M, a.N, a.K);
+  if (cfg < 0) cfg = select_gemm_config(a.M, a.N, a.K, a.batch);
   if (cfg >= ntiles * kNumGroups) return FP32GEMM_ERR_CONFIG;
   const GemmConfig &c = tiles[cfg / kNumGroups];
   return (int)c.launch[2 * ta + tb](a, vec4_ok(a, ta, tb), kGroups[cfg % kNumGroups], s);
@@ -260,7 +260,7 @@ int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha, const
   p.sB = transB ? (long long)kc : (long long)kc * ldb;
   p.sC = (long long)M * N;
   p.batch = chunks;
-  rc = run_gemm(model_gemm_config(M, N, chunks, nullptr), transA, transB, p, s);
+  rc = run_gemm(model_gemm_config(M, N, kc, chunks, nullptr), transA, transB, p, s);
   if (rc) return rc;
   // phase 2: C <- alpha * (sum of the planes, in order) + beta * C
   return (int)launch_splitk_reduce(workspace, chunks, M, N, alpha, beta, C, ldc, s);
@@ -302,7 +302,7 @@ const char *fp32gemm_config_name(int kind, int cfg) {
 }
 
 int fp32gemm_select_config(int kind, int M, int N, int K) {
-  if (kind == 0) return select_gemm_config(M, N, K);
+  if (kind == 0) return select_gemm_config(M, N, K, 1);
   if (kind == 1) return select_gemv_config(M, N, K);
   return FP32GEMM_ERR_CONFIG;
 }

@@ -146,11 +146,12 @@ constexpr int kGroups[kNumGroups] = {1, 2, 4, 8};
 int num_gemm_config_ids();
 const char *gemm_config_name(int id);
 
-// Per-shape table (generated by the tuning sweep) and size-class fallbacks.
-int select_gemm_config(int M, int N, int K);
-// The fallback model alone, for a grid of `mult` products of M x N (split-K
-// chunks); *rate receives the modelled TFLOP/s.
-int model_gemm_config(int M, int N, int mult, double *rate);
+// Per-shape table (generated by the tuning sweep; single products) and the
+// fallback model over the tiles of all `batch` entries.
+int select_gemm_config(int M, int N, int K, int batch);
+// The fallback model alone, for a grid of `mult` products of M x N x K (batch
+// entries or split-K chunks); *rate receives the modelled TFLOP/s.
+int model_gemm_config(int M, int N, int K, int mult, double *rate);
 // A tiled product as two launches over ranges of C: columns (dim 1) or rows
 // (dim 2) [0, first) in whole rounds of 256x256 tiles with configuration
 // main_cfg, the rest as a second product with its own configuration.

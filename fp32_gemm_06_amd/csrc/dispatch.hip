@@ -73,7 +73,13 @@ const char *gemm_config_name(int id) {
 // of up to 256 tiles (one 8-wave workgroup per CU at full rate) costs a whole
 // tile's work, of which M x N of the rounds' tile area is useful.  The 4-wave
 // 64x64 tile gets a further factor for fewer than four workgroups per CU,
-// which stops falling at one per CU (256 tiles).  Checked against the sweep,
+// which stops falling at one per CU (256 tiles).  Each tile also has a fixed
+// cost outside its K loop (filling the pipeline, writing C), priced as k0
+// extra steps of K: about 12 us per round of 256x256 tiles at 4092^3, the
+// time of 52 steps; 41 for the smaller tiles, from eight 2048 x 2048 x 128
+// products (80.5 us on 128x128 tiles against 83.5 on 256x256).  It moves
+// short-K products to the 128x128 tile: 8192^2 x 64 runs in 98 us there
+// against 103 on 256x256.  Checked against the sweep,
 // the estimate picks the measured best of the three tiles at 15 of the 16
 // swept shapes (at 2048^3 the two it confuses are 0.3% apart); tiny shapes
 // such as 128^3 get the 64x64 tile.
@@ -82,16 +88,17 @@ struct ModelTile {
   const char *name;
   int bm, bn;
   double full_rate;  // TFLOP/s with every CU busy
+  double k0;         // fixed cost per tile in steps of K
   bool small;        // 4-wave tile that needs several workgroups per CU
 };
 const ModelTile kModelTiles[] = {
-    {"256x256x32_w128x64_g4", 256, 256, 145.0, false},
-    {"128x128x32_w64x32_g4", 128, 128, 141.0, false},
-    {"64x64x32_w32x32_g4", 64, 64, 133.0, true},
+    {"256x256x32_w128x64_g4", 256, 256, 145.0, 52.0, false},
+    {"128x128x32_w64x32_g4", 128, 128, 141.0, 41.0, false},
+    {"64x64x32_w32x32_g4", 64, 64, 133.0, 41.0, true},
 };
 }  // namespace
 
-int model_gemm_config(int M, int N, int mult, double *rate_out) {
+int model_gemm_config(int M, int N, int K, int mult, double *rate_out) {
   int best = -1;
   double best_rate = -1.0;
   for (const ModelTile &c : kModelTiles) {
@@ -100,6 +107,7 @@ int model_gemm_config(int M, int N, int mult, double *rate_out) {
     // each round costs a whole tile's work per CU; only M x N x mult of it is useful
     double rate = c.full_rate / 256.0 * ((double)M * (double)N * mult) / (rounds * c.bm * c.bn);
     if (c.small && tiles < 1024.0) rate *= pow((tiles < 256.0 ? 256.0 : tiles) / 1024.0, 0.3);
+    rate *= (double)K / ((double)K + c.k0);
     const int id = find_gemm(c.name);
     if (id >= 0 && rate > best_rate) {
       best_rate = rate;
@@ -110,13 +118,26 @@ int model_gemm_config(int M, int N, int mult, double *rate_out) {
   return best >= 0 ? best : 0;
 }
 
-int select_gemm_config(int M, int N, int K) {
-  for (const ShapeEntry &e : kGemmTable)
-    if (e.M == M && e.N == N && e.K == K) {
-      const int id = find_gemm(e.name);
-      if (id >= 0) return id;
-    }
-  return model_gemm_config(M, N, 1, nullptr);
+int select_gemm_config(int M, int N, int K, int batch) {
+  if (batch == 1)
+    for (const ShapeEntry &e : kGemmTable)
+      if (e.M == M && e.N == N && e.K == K) {
+        const int id = find_gemm(e.name);
+        if (id >= 0) return id;
+      }
+  int best = model_gemm_config(M, N, K, batch, nullptr);
+  // With at most one 64x64 tile per CU (16 < tiles <= 256) and K long enough
+  // to split, the variant with two K groups and two slices per barrier keeps
+  // more waves issuing: 73.4 us against 76.4 plain at 192 x 4096 x 4096,
+  // 191 against 200 at 256 x 4096 x 11008, 22.1 against 22.8 at 1000^3.
+  // At 320..512 tiles the plain tile is 3% faster, and with K = 260 the
+  // split halves too few steps (9.1 against 8.2 us at 300 x 520 x 260).
+  const double tiles64 = (double)((M + 63) / 64) * (double)((N + 63) / 64) * batch;
+  if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 > 16.0 && tiles64 <= 256.0 && K >= 512) {
+    const int k2 = find_gemm("64x64x32_w32x32_k2_p2_g8");
+    if (k2 >= 0) best = k2;
+  }
+  return best;
 }
 
 // Tile quantization across two launches.  When the 256x256 tiles of a
@@ -135,7 +156,7 @@ RoundSplit plan_round_split(int M, int N, int K, int batch) {
   if (big < 0 || batch < 1 || M < 1 || N < 1 || K < 1) return r;
   const double work = 2.0 * (double)K * (double)batch;  // flop per element of C
   double rate = 0.0;
-  (void)model_gemm_config(M, N, batch, &rate);
+  (void)model_gemm_config(M, N, K, batch, &rate);
   double best = work * (double)M * (double)N / (rate * 1e6) * 0.99;  // us
   const long long tm = (M + 255) / 256, tn = (N + 255) / 256;
   for (int dim = 1; dim <= 2; ++dim) {
@@ -148,8 +169,8 @@ RoundSplit plan_round_split(int M, int N, int K, int batch) {
     const int m1 = dim == 1 ? M : first, n1 = dim == 1 ? first : N;
     const int m2 = dim == 1 ? M : M - first, n2 = dim == 1 ? N - first : N;
     double r1 = 0.0, r2 = 0.0;
-    (void)model_gemm_config(m1, n1, batch, &r1);
-    (void)model_gemm_config(m2, n2, batch, &r2);
+    (void)model_gemm_config(m1, n1, K, batch, &r1);
+    (void)model_gemm_config(m2, n2, K, batch, &r2);
     const double t = work * ((double)m1 * n1 / (r1 * 1e6) + (double)m2 * n2 / (r2 * 1e6)) + 3.0;
     if (t < best) {
       best = t;

@@ -78,7 +78,7 @@ int splitk_pick(int M, int N, int K) {
     const int chunks = splitk_chunk(K, s, &kc);
     if (chunks > 1 && kc < 256) break;
     double rate = 0.0;
-    model_gemm_config(M, N, chunks, &rate);
+    model_gemm_config(M, N, kc, chunks, &rate);
     double t = flops / (rate * 1e12);
     if (chunks > 1) t += (2.0 * chunks + 2.0) * M * (double)N * 4.0 / 5e12 + 3e-6;
     if (best_t < 0.0 || t < best_t) {

@@ -52,9 +52,9 @@ CASES = [
     (2048, 11008, 512, 0, 0, 1),
     (2048, 11008, 384, 1, 1, 1),
     (2048, 11008, 256, 0, 1, 1),
-    (3072, 8192, 1024, 0, 0, 2),
-    (3072, 8192, 1056, 1, 0, 2),
-    (3072, 8192, 1024, 1, 1, 2),
+    (2816, 8192, 1024, 0, 0, 2),
+    (2816, 8192, 1056, 1, 0, 2),
+    (2816, 8192, 1024, 1, 1, 2),
 ]
 
 
