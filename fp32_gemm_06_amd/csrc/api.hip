@@ -115,12 +115,14 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
 // ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N, K =
 // 1024..32000 (8 weight copies, one box): the skinny kernel is faster for
 // every M <= 32 (4096^2, M = 16: 23.4 against 99.7 us), and above that
-// while the tiled kernel has fewer than 256 tiles (N = 11008, M = 64: 94.8
-// against 104.3 us; M = 96, 344 tiles: 193 against 134).
+// while the tiled kernel has fewer than 160 tiles (4096^2, M = 128, 128
+// tiles: 63.3 against 75.3 us).  From 172 tiles on, the tiled kernel with
+// two K slices per barrier is faster (N = 11008, K = 4096, M = 48: 77.6
+// against 86.0 us).
 bool skinny_pays(const GemmArgs &a) {
   if (a.M <= 32) return true;
   const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
-  return tiles < 256;
+  return tiles < 160;
 }
 
 // The product on the kernel that suits it: M <= 8 on a GEMV kernel (row dots

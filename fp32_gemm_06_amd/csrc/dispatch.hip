@@ -126,16 +126,20 @@ int select_gemm_config(int M, int N, int K, int batch) {
         if (id >= 0) return id;
       }
   int best = model_gemm_config(M, N, K, batch, nullptr);
-  // With at most one 64x64 tile per CU (16 < tiles <= 256) and K long enough
-  // to split, the variant with two K groups and two slices per barrier keeps
-  // more waves issuing: 73.4 us against 76.4 plain at 192 x 4096 x 4096,
-  // 191 against 200 at 256 x 4096 x 11008, 22.1 against 22.8 at 1000^3.
-  // At 320..512 tiles the plain tile is 3% faster, and with K = 260 the
-  // split halves too few steps (9.1 against 8.2 us at 300 x 520 x 260).
+  // With at most one 64x64 tile per CU (16 < tiles <= 256) and K long enough,
+  // the variant that stages two K slices per barrier keeps two slices of
+  // loads in flight instead of one.  Where B comes from HBM (a weight read
+  // once per call) it is much faster: 74.3 us against 99.7 plain at
+  // 160 x 4096 x 4096, 195.6 against 259.1 at 256 x 4096 x 11008; with B
+  // already in the caches it is 2-8% faster (73.4 against 75.7 at
+  // 160 x 4096 x 4096).  The variant that also splits each slice between
+  // two groups of waves times the same with B cached but 8-13% slower from
+  // HBM.  At 320..512 tiles the plain tile is up to 3% faster, and with
+  // K = 260 the staging covers too few slices.
   const double tiles64 = (double)((M + 63) / 64) * (double)((N + 63) / 64) * batch;
   if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 > 16.0 && tiles64 <= 256.0 && K >= 512) {
-    const int k2 = find_gemm("64x64x32_w32x32_k2_p2_g8");
-    if (k2 >= 0) best = k2;
+    const int p2 = find_gemm("64x64x32_w32x32_p2_g8");
+    if (p2 >= 0) best = p2;
   }
   return best;
 }

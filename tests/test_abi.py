@@ -251,3 +251,22 @@ def test_round_split_plan():
         along = N if dim == 1 else M
         assert first % 256 == 0 and 0 < first < along
         assert (across * (first // 256) * b) % 256 == 0
+
+
+def test_model_choices():
+    """The fallback tile model on shapes the table does not list: short K
+    moves large products from 256x256 to 128x128 tiles (each tile's fixed
+    cost is a larger share), at most one 64x64 tile per CU takes the variant
+    with two K slices per barrier (K >= 512 only), more tiles keep the plain
+    64x64 tile, and a K too short to stage keeps it too."""
+    name = lambda *s: fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, *s))
+    assert name(8192, 4096, 4096).startswith("256x256x32_")
+    assert name(8192, 4096, 128).startswith("128x128x32_w64x32")
+    assert name(4096, 4096, 64).startswith("128x128x32_w64x32")
+    for shape in [(160, 4096, 4096), (192, 4096, 4096), (256, 4096, 11008), (1000, 1000, 1000),
+                  (200, 2000, 8000)]:
+        assert name(*shape) == "64x64x32_w32x32_p2_g8", shape
+    for shape in [(384, 4096, 4096), (320, 4096, 4096), (1100, 1100, 1100), (300, 520, 260)]:
+        assert name(*shape).startswith("64x64x32_w32x32_g"), shape
+    # tiny products keep the plain tile: 2 x 2 tiles
+    assert name(100, 100, 4096).startswith("64x64x32_w32x32_g")
