@@ -23,9 +23,11 @@
 //    stored N x K (TB): lane (q, c) reads stored rows n0 + 16 e + c along k
 //    (column block e), and a wave instruction reads 64 contiguous bytes of
 //    each of 16 consecutive rows;
-//  * X is staged per pass in LDS as [m][k] rows (stride ROWS + 4 floats, so
-//    the eight 16-byte reads an LDS cycle serves fall in distinct banks); one
-//    ds_read_b128 holds the A operand of four consecutive steps;
+//  * X is staged per pass in LDS as [m][k] rows with a stride of ROWS + 8
+//    floats; one ds_read_b128 holds the A operand of four consecutive steps.
+//    With a stride of ROWS + 4 the counters showed about two bank-conflict
+//    cycles per LDS instruction, with ROWS + 8 one in seventeen (ROWS + 16
+//    and + 20 as many as + 4); the time did not change;
 //  * M up to 16 MB rows, MB blocks of 16 sharing each W value; W runs D
 //    passes deep in registers and X one pass ahead through two LDS buffers,
 //    with the same branch-free masking as the GEMV: rows of X past M and
@@ -79,10 +81,14 @@ __global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a) {
   constexpr int MR = 16 * MB;               // row capacity of X
   constexpr int CW = 16 * NB;               // columns of W per workgroup
-  constexpr int ROWS = 1024 / (MB * NB);    // rows of K per pass
+  // rows of K per pass: 1024 / (MB NB), halved when MB NB <= 2, where a
+  // shorter pass gets W and X moving sooner (4096^2: M = 32, W stored N x K,
+  // 26.2 -> 24.1 us; M = 16, W stored K x N, 22.6 -> 21.5); with more blocks
+  // half the rows made M = 64 slower
+  constexpr int ROWS = (MB * NB <= 2 ? 512 : 1024) / (MB * NB);
   constexpr int RW = ROWS / kSkWaves;       // rows per wave per pass
   constexpr int G = RW / 4;                 // MFMA steps per wave per pass (rows per lane quarter)
-  constexpr int SK = ROWS + 4;              // LDS row stride of the X chunk, in floats
+  constexpr int SK = ROWS + 8;              // LDS row stride of the X chunk, in floats
   // accumulator sets: with few independent blocks, consecutive steps
   // alternate between sets so that no MFMA waits on the one before it
   constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
