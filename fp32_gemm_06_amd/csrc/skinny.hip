@@ -42,6 +42,12 @@ namespace {
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * 64;
 
+constexpr int pow2_floor(int v) {
+  int p = 1;
+  while (2 * p <= v) p *= 2;
+  return p;
+}
+
 template <int E> struct Vec { typedef float type __attribute__((ext_vector_type(E))); };
 template <> struct Vec<1> { typedef float type; };
 
@@ -85,7 +91,8 @@ skinny_kernel(GemmArgs a) {
   // shorter pass gets W and X moving sooner (4096^2: M = 32, W stored N x K,
   // 26.2 -> 24.1 us; M = 16, W stored K x N, 22.6 -> 21.5); with more blocks
   // half the rows made M = 64 slower
-  constexpr int ROWS = (MB * NB <= 2 ? 512 : 1024) / (MB * NB);
+  // (for MB = 3, 5, 6, 7 the power of two below).
+  constexpr int ROWS = pow2_floor((MB * NB <= 2 ? 512 : 1024) / (MB * NB));
   constexpr int RW = ROWS / kSkWaves;       // rows per wave per pass
   constexpr int G = RW / 4;                 // MFMA steps per wave per pass (rows per lane quarter)
   constexpr int SK = ROWS + 8;              // LDS row stride of the X chunk, in floats
@@ -94,6 +101,7 @@ skinny_kernel(GemmArgs a) {
   constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
   constexpr int XBUF = 2 * MR * SK, RED = kSkWaves * MR * CW;
   static_assert(G % 4 == 0, "A fragments are read four steps at a time");
+  static_assert(!TA || kSkThreads % MR == 0, "op(A) = A^T stages whole columns of X per thread group");
   static_assert(!TB || G % WV == 0, "stored-transposed W: whole vectors per pass");
   static_assert((XBUF > RED ? XBUF : RED) * 4 <= 160 * 1024, "fits in LDS");
   __shared__ __attribute__((aligned(16))) float xs[XBUF > RED ? XBUF : RED];
@@ -329,9 +337,14 @@ hipError_t launch_mb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
   const long long blocks = ((long long)a.N + 16 * NB - 1) / (16 * NB);
   if (blocks > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, (unsigned)a.batch), block(kSkThreads);
-  if (transA)
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, true, false, TB, WV>), grid, block, 0, s, a);
-  else if (xv)
+  if (transA) {
+    // 3, 5, 6 or 7 row blocks run op(A) = A only (their X staging for A^T
+    // would not divide evenly between the threads)
+    if constexpr (kSkThreads % (16 * MB) == 0)
+      hipLaunchKernelGGL((skinny_kernel<MB, NB, true, false, TB, WV>), grid, block, 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else if (xv)
     hipLaunchKernelGGL((skinny_kernel<MB, NB, false, true, TB, WV>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((skinny_kernel<MB, NB, false, false, TB, WV>), grid, block, 0, s, a);
@@ -364,9 +377,15 @@ hipError_t launch_nb(const GemmArgs &a, int transA, hipStream_t s) {
     if (a.M <= 32) return launch_mb<2, NB>(a, transA, xv, s);
   }
   if constexpr (NB <= 2) {
+    if (a.M <= 48 && !transA) return launch_mb<3, NB>(a, transA, xv, s);
     if (a.M <= 64) return launch_mb<4, NB>(a, transA, xv, s);
   }
-  if constexpr (NB == 1) return launch_mb<8, NB>(a, transA, xv, s);
+  if constexpr (NB == 1) {
+    if (a.M <= 80 && !transA) return launch_mb<5, NB>(a, transA, xv, s);
+    if (a.M <= 96 && !transA) return launch_mb<6, NB>(a, transA, xv, s);
+    if (a.M <= 112 && !transA) return launch_mb<7, NB>(a, transA, xv, s);
+    return launch_mb<8, NB>(a, transA, xv, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -393,9 +412,15 @@ hipError_t launch_tb_nb(const GemmArgs &a, int transA, hipStream_t s) {
     if (a.M <= 32) return launch_mb_tb<2, NB>(a, transA, xv, s);
   }
   if constexpr (NB <= 2) {
+    if (a.M <= 48 && !transA) return launch_mb_tb<3, NB>(a, transA, xv, s);
     if (a.M <= 64) return launch_mb_tb<4, NB>(a, transA, xv, s);
   }
-  if constexpr (NB == 1) return launch_mb_tb<8, NB>(a, transA, xv, s);
+  if constexpr (NB == 1) {
+    if (a.M <= 80 && !transA) return launch_mb_tb<5, NB>(a, transA, xv, s);
+    if (a.M <= 96 && !transA) return launch_mb_tb<6, NB>(a, transA, xv, s);
+    if (a.M <= 112 && !transA) return launch_mb_tb<7, NB>(a, transA, xv, s);
+    return launch_mb_tb<8, NB>(a, transA, xv, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -77,7 +77,7 @@ def test_transposed_x_huge_lda_falls_back(tb):
     assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"huge lda tb={tb}")
 
 
-WIDE_M = [9, 12, 13, 16, 17, 24, 25, 32, 33, 48, 64, 65, 100, 128]
+WIDE_M = [9, 12, 13, 16, 17, 24, 25, 32, 33, 40, 48, 49, 64, 65, 80, 96, 97, 100, 128]
 
 
 @pytest.mark.parametrize("M", WIDE_M)
@@ -131,7 +131,7 @@ def test_wide_rows_transposed_x(M):
 
 
 @pytest.mark.parametrize("ta", (0, 1))
-@pytest.mark.parametrize("M", [9, 16, 33, 64, 100, 128])
+@pytest.mark.parametrize("M", [9, 16, 33, 48, 64, 80, 96, 100, 128])
 def test_wide_rows_weight_transposed(ta, M):
     """op(B) = B^T (weight stored N x K) with M = 9..128: the skinny kernel's
     stored-row path, with 16-byte loads along k (aligned, K % 4 == 0) and
@@ -146,10 +146,10 @@ def test_wide_rows_weight_transposed(ta, M):
 
 
 def test_wide_rows_batched():
-    """Strided batches of M = 16, 27 and 70 entries in one skinny grid, both
-    weight layouts."""
+    """Strided batches of M = 16, 27, 45 and 70 entries in one skinny grid,
+    both weight layouts."""
     from test_transpose_batched import _case, run_batched
-    for M in (16, 27, 70):
+    for M in (16, 27, 45, 70):
         for tb in (0, 1):
             As, Bs, Cs = _case(7300 + M, M, 200, 300, batch=3)
             outs, ok = run_batched(0, tb, As, Bs, Cs, 1.0, 1.0, pads=(1, 2, 3), gaps=(7, 5, 3))
