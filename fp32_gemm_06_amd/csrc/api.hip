@@ -110,17 +110,17 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
   return run_gemm(-1, ta, tb, q, s);
 }
 
-// M = 9..128: the skinny MFMA kernel (N / 16 workgroups or more, each over
+// M = 9..128: the skinny MFMA kernel (N / 16 workgroups or fewer, each over
 // all of K), or the tiled kernel, whose 64x64 tiles number only
-// ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N, K =
-// 1024..32000 (8 weight copies, one box): the skinny kernel is faster for
-// every M <= 32 (4096^2, M = 16: 23.4 against 99.7 us), and above that
-// while the tiled kernel has fewer than 160 tiles (4096^2, M = 128, 128
-// tiles: 63.3 against 75.3 us).  From 172 tiles on, the tiled kernel with
-// two K slices per barrier is faster (N = 11008, K = 4096, M = 48: 77.6
-// against 86.0 us).
+// ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N =
+// 2048..16384, K = 4096 (cold weights, one box): the skinny kernel is faster
+// for every M <= 48 (4096^2, M = 16: 21.4 against 99.7 us; N = 11008, M =
+// 48: 71.7 against 77.8; N = 16384, M = 48: 73.2 against 82.5), and above
+// that while the tiled kernel has fewer than 160 tiles (4096^2, M = 128:
+// 59.4 against 75.3).  From 172 tiles on, the tiled kernel with two K slices
+// per barrier is faster (N = 11008, M = 64: 80.1 against 86.4 us).
 bool skinny_pays(const GemmArgs &a) {
-  if (a.M <= 32) return true;
+  if (a.M <= 48) return true;
   const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
   return tiles < 160;
 }

@@ -201,14 +201,12 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
   // widest stripe that still leaves about 160 workgroups or more.
   (void)K;
   if (M > 8) {
-    // The skinny MFMA kernel, with the same stripe-width rule as the GEMV:
-    // 64-column stripes (M <= 32) from N x batch = 10240, 32-column stripes
-    // (M <= 64) from 8192, else 16.  Measured: N = 11008, M = 16: 40.2 us
-    // on 64 columns against 69.5 on 16; N = K = 8192, M = 32: 65.3 on 32
-    // against 96.5 on 16; N = K = 4096: 16 columns best.
-    const char *mf = NB >= 160 * 64 && M <= 32   ? "mfma64_w8"
-                     : NB >= 256 * 32 && M <= 64 ? "mfma32_w8"
-                                                 : "mfma16_w8";
+    // The skinny MFMA kernel on the stripe width that needs the fewest
+    // rounds of workgroups, weighted by the wider stripes' cost (N = 11008,
+    // M = 16: 42.1 us on 64 columns against 62.7 on 16; N = 4608, M = 48:
+    // 39.7 on 32 against 56.5 on 16; N = 4096: 16 columns best).
+    const int nb = skinny_stripe_blocks(M, NB);
+    const char *mf = nb == 4 ? "mfma64_w8" : nb == 2 ? "mfma32_w8" : "mfma16_w8";
     const int id = find_gemv(mf);
     return id >= 0 ? id : 0;
   }

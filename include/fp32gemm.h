@@ -60,7 +60,7 @@ typedef struct ihipStream_t *fp32gemm_stream_t;
  * Argument checks: M, N, K >= 0; lda >= max(1, K); ldb >= max(1, N);
  * ldc >= max(1, N); A and B non-NULL when alpha != 0 and K > 0; C non-NULL
  * when M > 0 and N > 0.  M <= 8 is routed to the GEMV kernel (sgemv), and
- * M = 9..128 to the skinny MFMA kernel where it is the faster (M <= 32
+ * M = 9..128 to the skinny MFMA kernel where it is the faster (M <= 48
  * always, above that while the tiled kernel has fewer than 160 64x64 tiles);
  * larger M runs the LDS-tiled fp32 MFMA kernel with the tile configuration
  * that the per-shape table selects for (M, N, K).
