@@ -121,9 +121,10 @@ hipError_t launch_skinny32(const GemmArgs &a, int transA, hipStream_t s);
 hipError_t launch_skinny64(const GemmArgs &a, int transA, hipStream_t s);
 // The same for op(B) = B^T (W stored N x K), 16 stored rows of W per workgroup.
 hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s);
-// Stripe width of the skinny kernel in column blocks of 16 (1, 2 or 4) for M
-// rows over n_total = N x batch columns.
-int skinny_stripe_blocks(int M, long long n_total);
+// Stripe widths in blocks of 16 columns (1, 2 or 4) for batch products of N
+// columns: the skinny MFMA kernel's for M rows, and the column-stripe GEMV's.
+int skinny_stripe_blocks(int M, int N, int batch);
+int gemv_stripe_blocks(int N, int batch);
 
 // Small-M product with op(B) = B^T (B stored N x K): row-dot kernel.
 // rows_per_wave is 1 or 2; <= 0 picks from M.

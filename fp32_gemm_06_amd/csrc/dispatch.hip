@@ -184,6 +184,47 @@ RoundSplit plan_round_split(int M, int N, int K, int batch) {
   return r;
 }
 
+// Stripe width for a grid of one workgroup per stripe of 16 nb columns and
+// batch entry.  Such a workgroup's time hardly depends on N, so the grid
+// costs about its rounds of 256 workgroups (one per CU) times the time of
+// one workgroup, which grows with the width: cost[i] for 16 << i columns,
+// relative to 16.  The narrowest width reaches no lower estimate than a
+// wider one, so ties go to the narrower stripe.
+int stripe_blocks(int N, int batch, int widest, const double cost[3]) {
+  int best = 1;
+  double best_t = -1.0;
+  for (int i = 0, nb = 1; i < 3 && nb <= widest; ++i, nb *= 2) {
+    const long long wg = (long long)((N + 16 * nb - 1) / (16 * nb)) * (batch > 1 ? batch : 1);
+    const double t = (double)((wg + 255) / 256) * cost[i];
+    if (best_t < 0.0 || t < best_t) {
+      best_t = t;
+      best = nb;
+    }
+  }
+  return best;
+}
+
+// The skinny kernel: 32-column stripes hold M <= 64 and 64-column ones M <=
+// 32; a 32-column workgroup takes about 1.3 and a 64-column one 1.7 times as
+// long as a 16-column one (W stored K x N at N = 4096, M = 9..64).  Swept
+// over N = 2048..16384 and M = 9..64, this picks the fastest width at all 84
+// points; N = 4608 to 7168 had taken 16 columns and two rounds, 1.2-1.5x
+// slower than one round of 32.
+int skinny_stripe_blocks(int M, int N, int batch) {
+  static const double cost[3] = {1.0, 1.3, 1.7};
+  return stripe_blocks(N, batch, M <= 32 ? 4 : M <= 64 ? 2 : 1, cost);
+}
+
+// The column-stripe GEMV (M <= 8): 1.1 and 1.5 times the 16-column time for
+// 32 and 64 columns (N = 4096: 18.2, 20.2 and 27.9 us at M = 1).  N = 4608
+// to 7168 then runs on 32 columns (M = 1, N = 6144: 23.7 us against 35.0 on
+// 16) and N = 9216 on 64 (36.0 against 42.5 on 32); the sizes swept before
+// (N = 1024..65536 in powers of two, 11008, 32000) keep their widths.
+int gemv_stripe_blocks(int N, int batch) {
+  static const double cost[3] = {1.0, 1.1, 1.5};
+  return stripe_blocks(N, batch, 4, cost);
+}
+
 int select_gemv_config(int M, int N, int K) { return select_gemv_config_batched(M, N, K, 1); }
 
 int select_gemv_config_batched(int M, int N, int K, int batch) {
@@ -193,27 +234,23 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
         const int id = find_gemv(e.name);
         if (id >= 0) return id;
       }
-  // the workgroup count is the stripes of N times the batch entries
-  const long long NB = (long long)N * (batch > 1 ? batch : 1);
-  // Wider column stripes read longer runs of each row of W (64, 128 or 256
-  // bytes), which the memory system serves faster, but give fewer
-  // workgroups.  The sweep over N from 1024 to 65536 is fastest with the
-  // widest stripe that still leaves about 160 workgroups or more.
   (void)K;
   if (M > 8) {
-    // The skinny MFMA kernel on the stripe width that needs the fewest
-    // rounds of workgroups, weighted by the wider stripes' cost (N = 11008,
-    // M = 16: 42.1 us on 64 columns against 62.7 on 16; N = 4608, M = 48:
-    // 39.7 on 32 against 56.5 on 16; N = 4096: 16 columns best).
-    const int nb = skinny_stripe_blocks(M, NB);
+    // The skinny MFMA kernel (N = 11008, M = 16: 42.1 us on 64 columns
+    // against 62.7 on 16; N = 4608, M = 48: 39.7 on 32 against 56.5 on 16).
+    const int nb = skinny_stripe_blocks(M, N, batch);
     const char *mf = nb == 4 ? "mfma64_w8" : nb == 2 ? "mfma32_w8" : "mfma16_w8";
     const int id = find_gemv(mf);
     return id >= 0 ? id : 0;
   }
-  const char *name = NB >= 160 * 64   ? "c64_w8_u4"
-                     : NB >= 256 * 32 ? "c32_w8_u4"
-                     : M >= 4 && M <= 8 ? "c16_w4_u8"
-                                        : "c16_w8_u4";
+  // Wider column stripes read longer runs of each row of W (64, 128 or 256
+  // bytes), which the memory system serves faster, but give fewer
+  // workgroups.
+  const int nb = gemv_stripe_blocks(N, batch);
+  const char *name = nb == 4              ? "c64_w8_u4"
+                     : nb == 2            ? "c32_w8_u4"
+                     : M >= 4 && M <= 8   ? "c16_w4_u8"
+                                          : "c16_w8_u4";
   const int id = find_gemv(name);
   return id >= 0 ? id : 0;
 }

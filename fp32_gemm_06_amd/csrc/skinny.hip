@@ -424,32 +424,9 @@ hipError_t launch_tb_nb(const GemmArgs &a, int transA, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Column blocks per stripe (NB = 1, 2 or 4; 2 holds M <= 64 and 4 M <= 32)
-// for n_total = N x batch stripe columns.  A workgroup's time barely depends
-// on N, so what counts is how many rounds of 256 workgroups (one per CU)
-// the grid needs, times the cost of one workgroup: a 32-column stripe takes
-// about 1.3 and a 64-column one 1.7 times as long as a 16-column one (W
-// stored K x N at N = 4096, M = 9..64).  Swept over N = 2048..16384 and
-// M = 9..64, this picks the fastest width everywhere; N = 4608 to 7168 had
-// taken 16 columns and two rounds, 1.2-1.5x slower than one round of 32.
-int skinny_stripe_blocks(int M, long long n_total) {
-  static const double cost[3] = {1.0, 1.3, 1.7};
-  int best = 1;
-  double best_t = -1.0;
-  for (int i = 0, nb = 1; i < 3 && M <= 128 / nb; ++i, nb *= 2) {
-    const long long wg = (n_total + 16 * nb - 1) / (16 * nb);
-    const double t = (double)((wg + 255) / 256) * cost[i];
-    if (best_t < 0.0 || t < best_t) {
-      best_t = t;
-      best = nb;
-    }
-  }
-  return best;
-}
-
 hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s) {
   if (!skinny_supported(a, transA)) return hipErrorInvalidValue;
-  const int nb = skinny_stripe_blocks(a.M, (long long)a.N * a.batch);
+  const int nb = skinny_stripe_blocks(a.M, a.N, a.batch);
   if (nb == 4) return launch_tb_nb<4>(a, transA, s);
   if (nb == 2) return launch_tb_nb<2>(a, transA, s);
   return launch_tb_nb<1>(a, transA, s);
