@@ -10,7 +10,7 @@
 // memory pattern and does the arithmetic on the matrix cores:
 //
 //  * a workgroup owns a stripe of 16 NB columns of W (NB = 1, 2, 4; the
-//    library picks the widest stripe that still leaves enough workgroups)
+//    library picks the width whose grid needs the fewest rounds of 256)
 //    over the whole of K, and its 8 waves split each pass of ROWS rows of K;
 //    with 16-column stripes the two of a 128-byte line run on one XCD;
 //  * W values go straight from buffer loads into the B operand of
