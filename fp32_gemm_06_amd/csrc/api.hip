@@ -113,14 +113,22 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
 // M = 9..128: the skinny MFMA kernel (N / 16 workgroups or fewer, each over
 // all of K), or the tiled kernel, whose 64x64 tiles number only
 // ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N =
-// 2048..16384, K = 4096 (cold weights, one box): the skinny kernel is faster
-// for every M <= 48 (4096^2, M = 16: 21.4 against 99.7 us; N = 11008, M =
-// 48: 71.7 against 77.8; N = 16384, M = 48: 73.2 against 82.5), and above
-// that while the tiled kernel has fewer than 160 tiles (4096^2, M = 128:
-// 59.4 against 75.3).  From 172 tiles on, the tiled kernel with two K slices
-// per barrier is faster (N = 11008, M = 64: 80.1 against 86.4 us).
+// 4096..16384, K = 4096 (cold weights, both layouts of W, one box), the
+// skinny kernel is faster
+//  * for every M <= 48 (4096^2, M = 16: 21.4 against 99.7 us; N = 16384,
+//    M = 33: 68.7 against 83.7);
+//  * for M = 65..80, where the tiled kernel computes up to twice the rows
+//    (N = 11008, M = 80: 121 against 132; N = 16384: 123 against 134);
+//  * for M <= 96 while its 32-column stripes fit one round of workgroups
+//    (N = 8192, M = 96: 71.1 against 74.5);
+//  * while the tiled kernel has fewer than 160 tiles (4096^2, M = 128: 59.4
+//    against 75.3).
+// Otherwise the tiled kernel is (N = 11008, M = 64: 79.0 against 86.1 with
+// W stored N x K; M = 96: 132 against 138; N = 8192, M = 128: 79.0 against
+// 90.4).
 bool skinny_pays(const GemmArgs &a) {
-  if (a.M <= 48) return true;
+  if (a.M <= 48 || (a.M > 64 && a.M <= 80)) return true;
+  if (a.M <= 96 && (long long)a.N * a.batch <= 256 * 32) return true;
   const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;
   return tiles < 160;
 }

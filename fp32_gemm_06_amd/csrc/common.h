@@ -123,7 +123,7 @@ hipError_t launch_skinny64(const GemmArgs &a, int transA, hipStream_t s);
 hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s);
 // Stripe widths in blocks of 16 columns (1, 2 or 4) for batch products of N
 // columns: the skinny MFMA kernel's for M rows, and the column-stripe GEMV's.
-int skinny_stripe_blocks(int M, int N, int batch);
+int skinny_stripe_blocks(int M, int N, int batch, bool transposed_w);
 int gemv_stripe_blocks(int N, int batch);
 
 // Small-M product with op(B) = B^T (B stored N x K): row-dot kernel.

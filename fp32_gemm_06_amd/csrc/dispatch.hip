@@ -204,15 +204,23 @@ int stripe_blocks(int N, int batch, int widest, const double cost[3]) {
   return best;
 }
 
-// The skinny kernel: 32-column stripes hold M <= 64 and 64-column ones M <=
-// 32; a 32-column workgroup takes about 1.3 and a 64-column one 1.7 times as
-// long as a 16-column one (W stored K x N at N = 4096, M = 9..64).  Swept
-// over N = 2048..16384 and M = 9..64, this picks the fastest width at all 84
-// points; N = 4608 to 7168 had taken 16 columns and two rounds, 1.2-1.5x
-// slower than one round of 32.
-int skinny_stripe_blocks(int M, int N, int batch) {
-  static const double cost[3] = {1.0, 1.3, 1.7};
-  return stripe_blocks(N, batch, M <= 32 ? 4 : M <= 64 ? 2 : 1, cost);
+// The skinny kernel: 32-column stripes hold M <= 128 and 64-column ones
+// M <= 64.  One workgroup's time relative to a 16-column one grows with the
+// rows (W stored K x N, K = 4096, one round of workgroups each): 32 columns
+// 1.1x at M <= 16, 1.35x to M = 48, 1.45x at 64, 1.5x above; 64 columns
+// 1.65x to M = 32 and 2.2x above.  Swept over N = 2048..16384 and M = 9..128,
+// this picks the fastest width at every point but one (within 2%); N = 4608
+// to 7168 had taken 16 columns and two rounds, 1.2-1.5x slower than one
+// round of 32, and M = 65..128 at N = 8192 runs 1.28x faster on 32 columns.
+// Over W stored N x K the 64-column stripes cost more still above M = 32
+// (N = 16384, M = 33: 82.5 us against 76.7 on 32 columns), so there they
+// stop at M = 32.
+int skinny_stripe_blocks(int M, int N, int batch, bool transposed_w) {
+  static const double cost[4][3] = {
+      {1.0, 1.1, 1.65}, {1.0, 1.35, 1.7}, {1.0, 1.45, 2.2}, {1.0, 1.5, 9.9}};
+  const int row = M <= 16 ? 0 : M <= 48 ? 1 : M <= 64 ? 2 : 3;
+  const int widest = M <= (transposed_w ? 32 : 64) ? 4 : 2;
+  return stripe_blocks(N, batch, widest, cost[row]);
 }
 
 // The column-stripe GEMV (M <= 8): 1.1 and 1.5 times the 16-column time for
@@ -238,7 +246,7 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
   if (M > 8) {
     // The skinny MFMA kernel (N = 11008, M = 16: 42.1 us on 64 columns
     // against 62.7 on 16; N = 4608, M = 48: 39.7 on 32 against 56.5 on 16).
-    const int nb = skinny_stripe_blocks(M, N, batch);
+    const int nb = skinny_stripe_blocks(M, N, batch, false);
     const char *mf = nb == 4 ? "mfma64_w8" : nb == 2 ? "mfma32_w8" : "mfma16_w8";
     const int id = find_gemv(mf);
     return id >= 0 ? id : 0;

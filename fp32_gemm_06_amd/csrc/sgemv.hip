@@ -536,8 +536,8 @@ const GemvConfig *gemv_configs(int *count) {
       {"c32_w8_u8", 32, 8, 8, 8, &launch_gemv<32, 8, 8>},
       {"c64_w8_u4", 64, 8, 4, kGemvMaxRows, &launch_gemv<64, 8, 4>},
       {"mfma16_w8", 16, 8, 0, 128, &launch_skinny16},
-      {"mfma32_w8", 32, 8, 0, 64, &launch_skinny32},
-      {"mfma64_w8", 64, 8, 0, 32, &launch_skinny64},
+      {"mfma32_w8", 32, 8, 0, 128, &launch_skinny32},
+      {"mfma64_w8", 64, 8, 0, 64, &launch_skinny64},
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -87,12 +87,13 @@ __global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a) {
   constexpr int MR = 16 * MB;               // row capacity of X
   constexpr int CW = 16 * NB;               // columns of W per workgroup
-  // rows of K per pass: 1024 / (MB NB), halved when MB NB <= 2, where a
-  // shorter pass gets W and X moving sooner (4096^2: M = 32, W stored N x K,
-  // 26.2 -> 24.1 us; M = 16, W stored K x N, 22.6 -> 21.5); with more blocks
-  // half the rows made M = 64 slower
-  // (for MB = 3, 5, 6, 7 the power of two below).
-  constexpr int ROWS = pow2_floor((MB * NB <= 2 ? 512 : 1024) / (MB * NB));
+  // Rows of K per pass: the power of two at or below 1024 / (MB NB), halved
+  // when MB NB <= 2, where a shorter pass gets W and X moving sooner (4096^2:
+  // M = 32, W stored N x K, 26.2 -> 24.1 us; M = 16, W stored K x N, 22.6 ->
+  // 21.5; with more blocks half the rows made M = 64 slower), and at least
+  // 128, which keeps four MFMA steps per wave and pass.
+  constexpr int ROWS_FIT = pow2_floor((MB * NB <= 2 ? 512 : 1024) / (MB * NB));
+  constexpr int ROWS = ROWS_FIT < 128 ? 128 : ROWS_FIT;
   constexpr int RW = ROWS / kSkWaves;       // rows per wave per pass
   constexpr int G = RW / 4;                 // MFMA steps per wave per pass (rows per lane quarter)
   constexpr int SK = ROWS + 8;              // LDS row stride of the X chunk, in floats
@@ -360,10 +361,10 @@ hipError_t launch_mb_tb(const GemmArgs &a, int transA, bool xv, hipStream_t s) {
              : launch_mb<MB, NB, true, 1>(a, transA, xv, s);
 }
 
-// NB column blocks of 16 per workgroup; M <= 16 MB with MB * NB <= 8.
+// NB column blocks of 16 per workgroup; M <= 16 MB with MB * NB <= 16.
 template <int NB>
 hipError_t launch_nb(const GemmArgs &a, int transA, hipStream_t s) {
-  if (a.M < 1 || a.M > 128 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 256 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
   // NB > 1: W rows read NB floats at a time (B 4 NB-byte aligned, N and ldb
   // multiples of NB); otherwise the 16-column kernel runs
   if (NB > 1 && ((uintptr_t)a.B % (4 * NB) != 0 || a.N % NB != 0 || a.ldb % NB != 0 ||
@@ -375,12 +376,10 @@ hipError_t launch_nb(const GemmArgs &a, int transA, hipStream_t s) {
   if (a.M <= 16) return launch_mb<1, NB>(a, transA, xv, s);
   if constexpr (NB <= 4) {
     if (a.M <= 32) return launch_mb<2, NB>(a, transA, xv, s);
-  }
-  if constexpr (NB <= 2) {
     if (a.M <= 48 && !transA) return launch_mb<3, NB>(a, transA, xv, s);
     if (a.M <= 64) return launch_mb<4, NB>(a, transA, xv, s);
   }
-  if constexpr (NB == 1) {
+  if constexpr (NB <= 2) {
     if (a.M <= 80 && !transA) return launch_mb<5, NB>(a, transA, xv, s);
     if (a.M <= 96 && !transA) return launch_mb<6, NB>(a, transA, xv, s);
     if (a.M <= 112 && !transA) return launch_mb<7, NB>(a, transA, xv, s);
@@ -401,21 +400,19 @@ hipError_t launch_skinny16(const GemmArgs &a, int transA, hipStream_t s) {
   return launch_nb<1>(a, transA, s);
 }
 
-// W stored N x K, 16 NB stored rows per workgroup (M <= 16 MB, MB NB <= 8).
+// W stored N x K, 16 NB stored rows per workgroup (M <= 16 MB, MB NB <= 16).
 template <int NB>
 hipError_t launch_tb_nb(const GemmArgs &a, int transA, hipStream_t s) {
-  if (a.M < 1 || a.M > 128 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 256 / NB || (transA && a.lda > (1 << 17))) return hipErrorInvalidValue;
   const bool xv = !transA && (uintptr_t)a.A % 16 == 0 && a.lda % 4 == 0 && a.K % 4 == 0 &&
                   (a.batch == 1 || a.sA % 4 == 0);
   if (a.M <= 16) return launch_mb_tb<1, NB>(a, transA, xv, s);
   if constexpr (NB <= 4) {
     if (a.M <= 32) return launch_mb_tb<2, NB>(a, transA, xv, s);
-  }
-  if constexpr (NB <= 2) {
     if (a.M <= 48 && !transA) return launch_mb_tb<3, NB>(a, transA, xv, s);
     if (a.M <= 64) return launch_mb_tb<4, NB>(a, transA, xv, s);
   }
-  if constexpr (NB == 1) {
+  if constexpr (NB <= 2) {
     if (a.M <= 80 && !transA) return launch_mb_tb<5, NB>(a, transA, xv, s);
     if (a.M <= 96 && !transA) return launch_mb_tb<6, NB>(a, transA, xv, s);
     if (a.M <= 112 && !transA) return launch_mb_tb<7, NB>(a, transA, xv, s);
@@ -426,7 +423,7 @@ hipError_t launch_tb_nb(const GemmArgs &a, int transA, hipStream_t s) {
 
 hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s) {
   if (!skinny_supported(a, transA)) return hipErrorInvalidValue;
-  const int nb = skinny_stripe_blocks(a.M, a.N, a.batch);
+  const int nb = skinny_stripe_blocks(a.M, a.N, a.batch, true);
   if (nb == 4) return launch_tb_nb<4>(a, transA, s);
   if (nb == 2) return launch_tb_nb<2>(a, transA, s);
   return launch_tb_nb<1>(a, transA, s);

@@ -61,7 +61,8 @@ typedef struct ihipStream_t *fp32gemm_stream_t;
  * ldc >= max(1, N); A and B non-NULL when alpha != 0 and K > 0; C non-NULL
  * when M > 0 and N > 0.  M <= 8 is routed to the GEMV kernel (sgemv), and
  * M = 9..128 to the skinny MFMA kernel where it is the faster (M <= 48
- * always, above that while the tiled kernel has fewer than 160 64x64 tiles);
+ * and M = 65..80 always, M <= 96 up to N = 8192, otherwise while the tiled
+ * kernel has fewer than 160 64x64 tiles);
  * larger M runs the LDS-tiled fp32 MFMA kernel with the tile configuration
  * that the per-shape table selects for (M, N, K).
  */
@@ -205,7 +206,7 @@ const char *fp32gemm_config_name(int kind, int cfg);
 int fp32gemm_select_config(int kind, int M, int N, int K);
 
 /* The largest M a configuration runs (kind as above; -1 for an unknown id):
- * 8, 32 or 128 for the GEMV family, INT_MAX for the tiled family. */
+ * 8, 32, 64 or 128 for the GEMV family, INT_MAX for the tiled family. */
 int fp32gemm_config_max_rows(int kind, int cfg);
 
 /* Whether the tiled kernel runs this product (batch entries of M x N x K) as

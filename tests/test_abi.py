@@ -130,9 +130,10 @@ def test_gemv_batch_range(lib):
     assert set(rows) == {8, 32, 64, 128}
     for cfg, name in enumerate(names):
         # the 4-rows-per-lane, <= 8-wave GEMV configurations take 32 rows,
-        # the MFMA ones 32, 64 or 128 by stripe width, the others 8
+        # the MFMA ones 128 (16- and 32-column stripes) or 64 (64 columns),
+        # the others 8
         if name.startswith("mfma"):
-            assert rows[cfg] == {"16": 128, "32": 64, "64": 32}[name[4:6]], name
+            assert rows[cfg] == {"16": 128, "32": 128, "64": 64}[name[4:6]], name
         else:
             waves, unroll = (int(v[1:]) for v in name.split("_")[1:3])
             assert rows[cfg] == (32 if unroll == 4 and waves <= 8 else 8), name

@@ -84,7 +84,7 @@ WIDE_M = [9, 12, 13, 16, 17, 24, 25, 32, 33, 40, 48, 49, 64, 65, 80, 96, 97, 100
 def test_wide_rows_every_config(M):
     """M = 9..128: every configuration of the GEMV family that runs this M
     (vector-ALU stripes on row capacities up to 32, the skinny MFMA kernel on
-    16/32/64-column stripes up to 128/64/32 rows; rows past M masked), both
+    16/32/64-column stripes up to 128/128/64 rows; rows past M masked), both
     load paths, bit-exact, nothing written outside C; the configurations
     whose row limit is below M are refused."""
     require_gpu()
