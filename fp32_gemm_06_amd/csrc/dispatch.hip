@@ -141,6 +141,20 @@ int select_gemm_config(int M, int N, int K, int batch) {
     const int p2 = find_gemm("64x64x32_w32x32_p2_g8");
     if (p2 >= 0) best = p2;
   }
+  // With more 64x64 tiles than CUs, 32-row tiles (32 x 128, same area) cut
+  // the rows computed past M by up to half where M % 64 is 1..32.  They are
+  // taken when that saves a whole round of 256 tiles: 160 x 11008 x 4096
+  // (430 tiles instead of 516 on 192 padded rows) 142.4 us against 190.8,
+  // 96 x 13824 x 4096 134.6 against 142.4.  With the same rounds they gained
+  // at most 4% and lost up to 2% (352 x 4096 x 4096, 608 x 4096 x 4096,
+  // 288 x 11008 x 4096: their full rate is 2.7% lower, 1023 against 998 us
+  // at 4096^3).
+  if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 > 256.0) {
+    const long long t32 = (long long)((M + 31) / 32) * ((N + 127) / 128) * batch;
+    const long long rounds64 = ((long long)tiles64 + 255) / 256, rounds32 = (t32 + 255) / 256;
+    const int id = find_gemm("32x128x32_w32x32_g8");
+    if (id >= 0 && rounds32 < rounds64) best = id;
+  }
   return best;
 }
 

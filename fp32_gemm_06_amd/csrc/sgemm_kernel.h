@@ -539,4 +539,5 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
   X(64, 64, 32, 32, 32, 1, 1, 4)     \
   X(64, 64, 32, 32, 32, 1, 2, 2)     \
   X(64, 64, 32, 32, 32, 1, 4, 1)     \
-  X(64, 64, 32, 32, 32, 2, 2, 2)
+  X(64, 64, 32, 32, 32, 2, 2, 2)     \
+  X(32, 128, 32, 32, 32, 1, 1, 3)

@@ -271,3 +271,8 @@ def test_model_choices():
         assert name(*shape).startswith("64x64x32_w32x32_g"), shape
     # tiny products keep the plain tile: 2 x 2 tiles
     assert name(100, 100, 4096).startswith("64x64x32_w32x32_g")
+    # 32-row tiles where they save a round of 256 tiles (516 -> 430), not
+    # where the rounds stay the same
+    assert name(160, 11008, 4096) == "32x128x32_w32x32_g8"
+    for shape in [(96, 11008, 4096), (352, 4096, 4096), (288, 11008, 4096)]:
+        assert name(*shape).startswith("64x64x32_w32x32_g"), shape
