@@ -276,3 +276,27 @@ def test_model_choices():
     assert name(160, 11008, 4096) == "32x128x32_w32x32_g8"
     for shape in [(96, 11008, 4096), (352, 4096, 4096), (288, 11008, 4096)]:
         assert name(*shape).startswith("64x64x32_w32x32_g"), shape
+
+
+def test_stripe_width_by_rounds():
+    """Column-stripe and skinny widths: the narrowest stripe whose grid needs
+    the fewest rounds of 256 workgroups (weighted by the wider stripes' cost
+    per workgroup), within each configuration's row limit."""
+    name = lambda *s: fg.fp32gemm_config_name(1, fg.fp32gemm_select_config(1, *s))
+    # M <= 8: 16 columns while one round holds the grid (N <= 4096), then 32, then 64
+    assert name(1, 4096, 4096) == "c16_w8_u4"
+    assert name(4, 4096, 4096) == "c16_w4_u8"
+    for N in (4608, 6144, 7168):
+        assert name(1, N, 4096) == "c32_w8_u4", N
+    assert name(1, 9216, 4096) == "c64_w8_u4"
+    assert name(8, 16384, 4096) == "c64_w8_u4"
+    # skinny kernel: 64-column stripes up to M = 64, 32-column up to 128
+    assert name(16, 4096, 4096) == "mfma16_w8"
+    assert name(48, 4608, 4096) == "mfma32_w8"
+    assert name(48, 11008, 4096) == "mfma64_w8"
+    assert name(80, 8192, 4096) == "mfma32_w8"
+    assert name(80, 11008, 4096) == "mfma16_w8"   # 3 rounds of 16 against 2 of 32 at 1.5x
+    assert name(128, 16384, 4096) == "mfma32_w8"
+    for M in (65, 100, 128):
+        cfg = fg.fp32gemm_select_config(1, M, 16384, 4096)
+        assert fg.fp32gemm_config_max_rows(1, cfg) >= M
