@@ -119,9 +119,10 @@ def test_wide_rows_routed(M):
             assert_parity(got, ref, bnd, f"M={M} N={N} K={K} {family}")
 
 
-@pytest.mark.parametrize("M", [10, 20, 32, 100])
+@pytest.mark.parametrize("M", [10, 20, 32, 48, 80, 100])
 def test_wide_rows_transposed_x(M):
-    """op(A) = A^T with M = 9..128: the skinny kernel reads X with swapped strides."""
+    """op(A) = A^T with M = 9..128: the skinny kernel reads X with swapped strides
+    (M = 48 and 80 round up to 4 and 8 row blocks: 3 and 5 take op(A) = A only)."""
     from test_transpose_batched import _case, run_batched
     N, K = 530, 3001
     As, Bs, Cs = _case(7200 + M, M, N, K)
@@ -157,3 +158,19 @@ def test_wide_rows_batched():
             for b in range(3):
                 assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 1.0),
                                 f"M={M} tb={tb} entry {b}")
+
+
+@pytest.mark.parametrize("tb", (0, 1))
+@pytest.mark.parametrize("M,offset", [(48, 0), (80, 0), (48, 1), (80, 1)])
+def test_wide_rows_batched_wide_stripes(tb, M, offset):
+    """Four entries of M x 4096 x 300: the grid of 16-column stripes takes four
+    rounds, so the skinny kernel runs 64-column stripes (M = 48, W stored
+    K x N) or 32-column ones; one float off a 16-byte boundary, the weight is
+    read a float at a time (stored N x K) or on 16-column stripes (K x N)."""
+    from test_transpose_batched import _case, run_batched
+    As, Bs, Cs = _case(7500 + M + tb + offset, M, 4096, 300, batch=4)
+    outs, ok = run_batched(0, tb, As, Bs, Cs, 1.0, 0.5, offset=offset)
+    assert ok, "write outside C"
+    for b in range(4):
+        assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5),
+                        f"M={M} tb={tb} offset={offset} entry {b}")
