@@ -113,7 +113,7 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
 // M = 9..128: the skinny MFMA kernel (N / 16 workgroups or fewer, each over
 // all of K), or the tiled kernel, whose 64x64 tiles number only
 // ceil(M / 64) * ceil(N / 64) and each walk all of K.  Measured over N =
-// 4096..16384, K = 4096 (cold weights, both layouts of W, one box), the
+// 4096..16384, K = 4096 (cold weights, both layouts of W, one GPU), the
 // skinny kernel is faster
 //  * for every M <= 48 (4096^2, M = 16: 21.4 against 99.7 us; N = 16384,
 //    M = 33: 68.7 against 83.7);

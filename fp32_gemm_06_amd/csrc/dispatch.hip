@@ -165,7 +165,7 @@ int select_gemm_config(int M, int N, int K, int batch) {
 // of 256x256 tiles and the rest, run as a second product with its own tile,
 // keeps most of the work on the fast tile.  The model above prices both
 // launches, plus 3 us for the second one; the split is taken when it is
-// estimated at least 1% faster.  Measured (one box, 18 shapes the model
+// estimated at least 1% faster.  Measured (one GPU, 18 shapes the model
 // flags): never slower, and 2-4% faster where the rest or the single launch
 // falls to the 64x64 tile (2048 x 11008 x 4096: 1357 -> 1308 us).
 RoundSplit plan_round_split(int M, int N, int K, int batch) {

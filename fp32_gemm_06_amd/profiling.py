@@ -112,7 +112,7 @@ def summarize(run_dir, prefix, command, timed=(100, 400)):
             continue
         s = stats[sk]
         lines = [f"# {tag}: rocprofv3 summary", "", f"Kernel: `{sk}`", "",
-                 "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+                 "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
                  f"Kernel source hash: `{source_hash(files)}`", "",
                  "| quantity | value |", "|---|---|",
                  f"| dispatches traced | {s['calls']} |",
