@@ -155,6 +155,15 @@ int select_gemm_config(int M, int N, int K, int batch) {
     const int id = find_gemm("32x128x32_w32x32_g8");
     if (id >= 0 && rounds32 < rounds64) best = id;
   }
+  // From two rounds of 64x64 tiles on, the same tile built from 16x16x4
+  // blocks (four accumulator chains per wave instead of one) is faster:
+  // 768 x 4096 x 4096 189.4 us against 203.9, 4096 x 2816 x 4096 666.4
+  // against 695.2, 3000^3 406.7 against 424.4; between one and two rounds it
+  // is about 3% slower (384 x 4096 x 4096 131.5 against 128.3).
+  if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 >= 512.0) {
+    const int id = find_gemm("64x64x32_w32x32_m16_g8");
+    if (id >= 0) best = id;
+  }
   return best;
 }
 

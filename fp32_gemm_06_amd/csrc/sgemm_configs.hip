@@ -12,11 +12,11 @@ const GemmConfig *gemm_configs(int *count) {
   // Names: BMxBNxBK_wWMxWN, then _k2 when two wave groups split K and _p2 /
   // _p4 for K slices per barrier.
   struct Shape {
-    int bm, bn, bk, wm, wn, ks, p, occ;
+    int bm, bn, bk, wm, wn, ks, p, occ, mf;
   };
   static const std::vector<std::string> names = [] {
     const Shape shapes[] = {
-#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC) {BM, BN, BK, WM, WN, KS, P, OCC},
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC, MF) {BM, BN, BK, WM, WN, KS, P, OCC, MF},
         FP32GEMM_TILES(FP32GEMM_ROW)
 #undef FP32GEMM_ROW
     };
@@ -26,13 +26,14 @@ const GemmConfig *gemm_configs(int *count) {
                       "_w" + std::to_string(t.wm) + "x" + std::to_string(t.wn);
       if (t.ks > 1) s += "_k" + std::to_string(t.ks);
       if (t.p > 1) s += "_p" + std::to_string(t.p);
+      if (t.mf == 16) s += "_m16";
       n.push_back(s);
     }
     return n;
   }();
   static const std::vector<GemmConfig> table = [] {
     const Shape shapes[] = {
-#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC) {BM, BN, BK, WM, WN, KS, P, OCC},
+#define FP32GEMM_ROW(BM, BN, BK, WM, WN, KS, P, OCC, MF) {BM, BN, BK, WM, WN, KS, P, OCC, MF},
         FP32GEMM_TILES(FP32GEMM_ROW)
 #undef FP32GEMM_ROW
     };

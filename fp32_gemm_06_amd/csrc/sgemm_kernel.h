@@ -17,7 +17,8 @@
 //  * each 64-lane wave owns a WM x WN sub-tile of 32 x 32 blocks, the CDNA4
 //    counterpart of warp tiling with per-thread register blocks ("CUDA 矩阵乘
 //    法优化", sections "6. Kernel 5" and "9. Kernel 10: 线程束级分块"); the
-//    outer product becomes v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate);
+//    outer product becomes v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate),
+//    or, for tiles built from 16 x 16 blocks (MF = 16), v_mfma_f32_16x16x4_f32;
 //  * slice k+1 is fetched while the matrix cores work on slice k, with two
 //    LDS buffers and one barrier per slice (double buffering, "11. 探索未尽与
 //    总结"; the two-barrier rule of "GPU GEMM 优化完全拆解（一）", section
@@ -45,6 +46,11 @@
 // a lane's values for four consecutive steps next to each other in LDS (one
 // ds_read_b128); an MC operand has the 32 lanes of a half reading 32
 // consecutive floats of one k-row (one ds_read_b32 per step).
+// For v_mfma_f32_16x16x4_f32 lane l supplies A[l % 16][k] and B[k][l % 16]
+// with k = l / 16 of the instruction's four; lane quarter q takes
+// k = 16 (q % 2) + 8 (q / 2) + step of a 32-wide slice, which keeps four
+// steps of a KC operand in one chunk and puts the quarters that an LDS cycle
+// serves together on the two sides of an MC tile's k-half gap.
 #pragma once
 
 #include "common.h"
@@ -58,20 +64,25 @@ namespace {
 // P > 1 (128-bit path): P K slices per barrier, i.e. stages of P slices in
 // 2 P LDS buffers, the next stage in flight during the current one (the
 // 32-bit staged path always uses one slice per barrier).
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int KS_ = 1, int P_ = 1>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int KS_ = 1, int P_ = 1, int MF_ = 32>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KS = KS_, P = P_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KS = KS_, P = P_, MF = MF_;
   static constexpr int WAVES_N = BN / WN;
   static constexpr int WT = (BM / WM) * WAVES_N;  // waves per K group
   static constexpr int WAVES = WT * KS;
   static constexpr int NT = WAVES * 64;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int NGW = BK / 8 / KS;  // step groups per wave per slice
-  static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
+  static constexpr int TM = WM / MF, TN = WN / MF;
+  static constexpr int NGW = BK / (MF == 32 ? 8 : 16) / KS;  // step groups per wave per slice
+  static constexpr int ACCN = MF == 32 ? 16 : 4;             // accumulator floats per block
+  static_assert(MF == 32 || (MF == 16 && BK == 32), "16x16x4 blocks take 32-wide K slices");
+  static_assert(BM % WM == 0 && BN % WN == 0 && WM % MF == 0 && WN % MF == 0, "wave tiling");
   static_assert(BK == 16 || BK == 32, "K slice of 16 or 32");
   static_assert(KS >= 1 && NGW >= 2 && NGW % 2 == 0, "fragment double buffering needs an even group count");
   static_assert(P >= 1 && P <= 4, "one to four K slices per barrier");
 };
+
+template <int MF> struct AccOf { typedef floatx16 type; };
+template <> struct AccOf<16> { typedef floatx4 type; };
 
 // Chunk swizzle of row r of a KC tile (float4 chunks of a BK-float row).
 // Checked exhaustively to keep ds_read_b128 of 32 consecutive rows at one
@@ -160,6 +171,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   const int kg = wave / T::WT, wt = wave % T::WT;  // K group; wave inside the group
   const int wm = wt / T::WAVES_N, wn = wt % T::WAVES_N;
   const int l32 = lane & 31, half = lane >> 5;
+  const int c16 = lane & 15, q4 = lane >> 4;
 
   const int rows = a.M - m0;  // valid rows of this tile (may exceed BM)
   const int cols = a.N - n0;
@@ -260,11 +272,12 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
-  floatx16 acc[T::TM][T::TN];
+  typedef typename AccOf<T::MF>::type acc_t;
+  acc_t acc[T::TM][T::TN];
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j) acc[i][j] = floatx16{};
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = acc_t{};
 
   // Operand fragments of one group of four MFMA steps: per 32-wide block,
   // this lane's four k values (k = half * BK/2 + 4g + step).
@@ -272,12 +285,51 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     float a[T::TM][4];
     float b[T::TN][4];
   };
-  const int ar = wm * T::WM + l32;  // this lane's row of block 0 along m
-  const int br = wn * T::WN + l32;  // ... along n
-  const int asw = kc_swizzle<BK>(ar), bsw = kc_swizzle<BK>(br);  // same for every 32-block
+  constexpr int MF = T::MF;
+  const int lr = MF == 32 ? l32 : c16;
+  const int ar = wm * T::WM + lr;  // this lane's row of block 0 along m
+  const int br = wn * T::WN + lr;  // ... along n
+  const int asw = kc_swizzle<BK>(ar), bsw = kc_swizzle<BK>(br);  // same for every block
+  // 16x16x4 blocks: lane quarter q takes k = 16 (q % 2) + 8 (q / 2) + step
+  // of the slice's 8 steps, so a KC read of four steps is one chunk and the
+  // quarters of an MC read fall in different k-halves (the 32-float gap).
+  const int kq = 16 * (q4 & 1) + 8 * (q4 >> 1);
   auto read_frag = [&](const float *buf, int g, Frag &f) {
     const float *As = buf;
     const float *Bs = buf + OA::FLOATS;
+    if constexpr (MF == 16) {
+      if constexpr (KCA) {
+        const float *pa = As + ar * BK + 4 * (((kq >> 2) + g) ^ asw);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+          const floatx4 v = *reinterpret_cast<const floatx4 *>(pa + i * 16 * BK);
+#pragma unroll
+          for (int st = 0; st < 4; ++st) f.a[i][st] = v[st];
+        }
+      } else {
+        const float *pa = As + (kq + 4 * g) * BM + (q4 & 1) * 32 + ar;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int i = 0; i < T::TM; ++i) f.a[i][st] = pa[st * BM + i * 16];
+      }
+      if constexpr (KCB) {
+        const float *pb = Bs + br * BK + 4 * (((kq >> 2) + g) ^ bsw);
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+          const floatx4 v = *reinterpret_cast<const floatx4 *>(pb + j * 16 * BK);
+#pragma unroll
+          for (int st = 0; st < 4; ++st) f.b[j][st] = v[st];
+        }
+      } else {
+        const float *pb = Bs + (kq + 4 * g) * BN + (q4 & 1) * 32 + br;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int j = 0; j < T::TN; ++j) f.b[j][st] = pb[st * BN + j * 16];
+      }
+      return;
+    }
     if constexpr (KCA) {
       const float *pa = As + ar * BK + 4 * ((half * (BK / 8) + g) ^ asw);
 #pragma unroll
@@ -316,7 +368,10 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
       for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][st], f.b[j][st], acc[i][j], 0, 0, 0);
+          if constexpr (MF == 16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][st], f.b[j][st], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][st], f.b[j][st], acc[i][j], 0, 0, 0);
   };
 
   // ---- main loop: one barrier per K slice ---------------------------------
@@ -421,7 +476,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   // The last slice ended with a barrier after every LDS read of the loop, so
   // the buffers are free.  Layout: [group - 1][wave in group][block][v][lane].
   if constexpr (T::KS > 1) {
-    constexpr int PER = T::TM * T::TN * 16 * 64;  // floats per wave
+    constexpr int PER = T::TM * T::TN * T::ACCN * 64;  // floats per wave
     static_assert((T::KS - 1) * T::WT * PER <= 2 * STAGE, "K-group sums fit in the LDS buffers");
     if (kg > 0) {
       float *red = lds + ((kg - 1) * T::WT + wt) * PER + lane;
@@ -430,7 +485,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) red[((i * T::TN + j) * 16 + v) * 64] = acc[i][j][v];
+          for (int v = 0; v < T::ACCN; ++v) red[((i * T::TN + j) * T::ACCN + v) * 64] = acc[i][j][v];
     }
     __syncthreads();
     if (kg > 0) return;
@@ -442,7 +497,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] += red[((i * T::TN + j) * 16 + v) * 64];
+          for (int v = 0; v < T::ACCN; ++v) acc[i][j][v] += red[((i * T::TN + j) * T::ACCN + v) * 64];
     }
   }
 
@@ -453,9 +508,11 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   // applied in registers before the only store of C.
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(Cg + (size_t)m0 * a.ldc + n0);
   const float alpha = a.alpha, beta = a.beta;
+  // (16 x 16 blocks: register v of lane (q, c) holds row 4 q + v, column c.)
   auto c_off = [&](int i, int j, int v) -> uint32_t {
-    const int row = wm * T::WM + i * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-    const int col = wn * T::WN + j * 32 + l32;
+    const int row = MF == 32 ? wm * T::WM + i * 32 + 8 * (v / 4) + 4 * half + (v % 4)
+                             : wm * T::WM + i * 16 + 4 * q4 + v;
+    const int col = wn * T::WN + j * MF + lr;
     return (row < rows && col < cols) ? (uint32_t)(row * a.ldc + col) * 4u : kOob;
   };
   float bj[T::TN];  // this lane's bias value per 32-column block
@@ -465,7 +522,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     const __amdgpu_buffer_rsrc_t rs_bias = make_rsrc(a.bias + n0);
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
-      const int col = wn * T::WN + j * 32 + l32;
+      const int col = wn * T::WN + j * MF + lr;
       const uint32_t off = col < cols ? (uint32_t)col * 4u : kOob;
       bj[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_bias, off, 0, 0));
     }
@@ -478,12 +535,12 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) {
-        float c0[16];
+        float c0[T::ACCN];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
+        for (int v = 0; v < T::ACCN; ++v)
           c0[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_c, c_off(i, j, v), 0, 0));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < T::ACCN; ++v) {
           const float out = finish(alpha * acc[i][j][v] + beta * c0[v], j);
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
         }
@@ -494,7 +551,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
       for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < T::ACCN; ++v) {
           const float out = finish(alpha * acc[i][j][v], j);
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
         }
@@ -526,18 +583,19 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
 // <= 160 KB per workgroup, <= 512 registers per lane); the occupancy column
 // comes from the compiler's LDS and register counts.
 #define FP32GEMM_TILES(X)             \
-  X(256, 256, 32, 128, 64, 1, 1, 1)  \
-  X(256, 256, 16, 128, 64, 1, 1, 1)  \
-  X(256, 128, 32, 64, 64, 1, 1, 1)   \
-  X(128, 256, 32, 64, 64, 1, 1, 1)   \
-  X(128, 128, 32, 64, 32, 1, 1, 2)   \
-  X(256, 128, 32, 128, 64, 1, 1, 1)  \
-  X(256, 128, 16, 128, 64, 1, 1, 1)  \
-  X(128, 256, 32, 64, 128, 1, 1, 1)  \
-  X(128, 128, 32, 64, 64, 1, 1, 2)   \
-  X(128, 128, 16, 64, 64, 1, 1, 3)   \
-  X(64, 64, 32, 32, 32, 1, 1, 4)     \
-  X(64, 64, 32, 32, 32, 1, 2, 2)     \
-  X(64, 64, 32, 32, 32, 1, 4, 1)     \
-  X(64, 64, 32, 32, 32, 2, 2, 2)     \
-  X(32, 128, 32, 32, 32, 1, 1, 3)
+  X(256, 256, 32, 128, 64, 1, 1, 1, 32)  \
+  X(256, 256, 16, 128, 64, 1, 1, 1, 32)  \
+  X(256, 128, 32, 64, 64, 1, 1, 1, 32)   \
+  X(128, 256, 32, 64, 64, 1, 1, 1, 32)   \
+  X(128, 128, 32, 64, 32, 1, 1, 2, 32)   \
+  X(256, 128, 32, 128, 64, 1, 1, 1, 32)  \
+  X(256, 128, 16, 128, 64, 1, 1, 1, 32)  \
+  X(128, 256, 32, 64, 128, 1, 1, 1, 32)  \
+  X(128, 128, 32, 64, 64, 1, 1, 2, 32)   \
+  X(128, 128, 16, 64, 64, 1, 1, 3, 32)   \
+  X(64, 64, 32, 32, 32, 1, 1, 4, 32)     \
+  X(64, 64, 32, 32, 32, 1, 2, 2, 32)     \
+  X(64, 64, 32, 32, 32, 1, 4, 1, 32)     \
+  X(64, 64, 32, 32, 32, 2, 2, 2, 32)     \
+  X(32, 128, 32, 32, 32, 1, 1, 3, 32)    \
+  X(64, 64, 32, 32, 32, 1, 1, 4, 16)

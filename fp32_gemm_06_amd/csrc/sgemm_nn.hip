@@ -2,7 +2,7 @@
 #include "sgemm_kernel.h"
 
 namespace fp32gemm {
-#define FP32GEMM_LAUNCHER(BM, BN, BK, WM, WN, KS, P, OCC) &launch<Tile<BM, BN, BK, WM, WN, KS, P>, false, false>,
+#define FP32GEMM_LAUNCHER(BM, BN, BK, WM, WN, KS, P, OCC, MF) &launch<Tile<BM, BN, BK, WM, WN, KS, P, MF>, false, false>,
 // Fills out[] with this combination's launchers in tile-list order (a host
 // function, so the device pass does not try to emit host function pointers).
 void launchers_nn(GemmLaunchFn *out) {

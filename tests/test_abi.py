@@ -274,8 +274,12 @@ def test_model_choices():
     # 32-row tiles where they save a round of 256 tiles (516 -> 430), not
     # where the rounds stay the same
     assert name(160, 11008, 4096) == "32x128x32_w32x32_g8"
-    for shape in [(96, 11008, 4096), (352, 4096, 4096), (288, 11008, 4096)]:
+    # 16x16x4 blocks from two rounds of 64x64 tiles on
+    assert name(768, 4096, 4096) == "64x64x32_w32x32_m16_g8"
+    assert name(1100, 1100, 1100).startswith("64x64x32_w32x32_g")
+    for shape in [(96, 11008, 4096), (352, 4096, 4096)]:
         assert name(*shape).startswith("64x64x32_w32x32_g"), shape
+    assert name(288, 11008, 4096) == "64x64x32_w32x32_m16_g8"
 
 
 def test_stripe_width_by_rounds():
