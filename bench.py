@@ -223,7 +223,42 @@ def main():
             "call": "sgemm_ex(transA=0, transB=1)", "us_per_call": round(tus, 3),
             "GB/s": round(tbps, 1), "frac": round(tbps / acc.PEAK_HBM_GBPS, 4),
             "traffic": stored_traffic("gemv_nt_m1_4096", GEMV_SOURCES)}
-        del dWt
+
+        # the other decode batch sizes of the workload, both weight layouts,
+        # the same rotating weight copies
+        def timed_calls(fn):
+            for i in range(32):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.gemv_steps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.gemv_steps * 1e3
+
+        dWk = [dWt[0].t().contiguous()]
+        for _ in range(nbuf - 1):
+            dWk.append(dWk[0].clone())
+        batch_rows = []
+        for name in ("decode_m4_4096", "decode_m8_4096"):
+            bw = inputs.WORKLOADS[name]
+            bX = torch.from_numpy(inputs.make(bw)[0]).to(dev)
+            bY = torch.zeros((bw.M, bw.N), dtype=torch.float32, device=dev)
+            nn_us = timed_calls(lambda i: check(fg.sgemv(
+                bw.M, bw.N, bw.K, bw.alpha, bX, bw.K, dWk[i % nbuf], bw.N, bw.beta, bY, bw.N, sp)))
+            nt_us = timed_calls(lambda i: check(fg.sgemm_ex(
+                0, 1, bw.M, bw.N, bw.K, bw.alpha, bX, bw.K, dWt[i % nbuf], bw.K, bw.beta, bY, bw.N,
+                sp)))
+            bbytes = acc.algorithmic_bytes(bw.M, bw.N, bw.K, bw.beta)
+            batch_rows.append({
+                "workload": name, "M": bw.M,
+                "weight_stored_KxN": {"us_per_call": round(nn_us, 3),
+                                      "GB/s": round(bbytes / (nn_us * 1e-6) / 1e9, 1)},
+                "weight_stored_NxK": {"us_per_call": round(nt_us, 3),
+                                      "GB/s": round(bbytes / (nt_us * 1e-6) / 1e9, 1)}})
+        gemv["decode_batch"] = batch_rows
+        del dWt, dWk
 
     # ---------------- CPU oracle on a bounded sample ----------------
     cpu = None
