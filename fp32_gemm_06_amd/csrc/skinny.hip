@@ -51,18 +51,19 @@ constexpr int pow2_floor(int v) {
 template <int E> struct Vec { typedef float type __attribute__((ext_vector_type(E))); };
 template <> struct Vec<1> { typedef float type; };
 
-// One raw buffer load of E floats (E = 1, 2, 4) at voffset + soffset bytes.
-template <int E>
+// One raw buffer load of E floats (E = 1, 2, 4) at voffset + soffset bytes,
+// with cache policy AUX.
+template <int E, int AUX = 0>
 __device__ __forceinline__ typename Vec<E>::type load_vec(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                                          int soff) {
   if constexpr (E == 4)
     return __builtin_bit_cast(typename Vec<4>::type,
-                              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, AUX));
   else if constexpr (E == 2)
     return __builtin_bit_cast(typename Vec<2>::type,
-                              __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+                              __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, AUX));
   else
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, AUX));
 }
 
 template <int E>
@@ -102,7 +103,8 @@ skinny_kernel(GemmArgs a) {
   constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
   constexpr int XBUF = 2 * MR * SK, RED = kSkWaves * MR * CW;
   static_assert(G % 4 == 0, "A fragments are read four steps at a time");
-  static_assert(!TA || kSkThreads % MR == 0, "op(A) = A^T stages whole columns of X per thread group");
+  static_assert(!TA || kSkThreads % MR == 0,
+                "op(A) = A^T stages whole columns of X per thread group");
   static_assert(!TB || G % WV == 0, "stored-transposed W: whole vectors per pass");
   static_assert((XBUF > RED ? XBUF : RED) * 4 <= 160 * 1024, "fits in LDS");
   __shared__ __attribute__((aligned(16))) float xs[XBUF > RED ? XBUF : RED];
@@ -159,13 +161,15 @@ skinny_kernel(GemmArgs a) {
         // WV == 4: K % 4 == 0 and kk + 4 q is a multiple of 4, so the four k
         // are all inside K or all past it
         const int e = l / (WL / NB), kk = kstep(l % (WL / NB) * WV);
+        // (the default cache policy: with the non-temporal bit the halves of
+        // a line read by consecutive loads cost up to 13% at N = 11008)
         wv[l] = load_vec<WV>(rw, r0 + 4 * q + kk < K ? w_lane[e] : kOob,
                              (16 * e * a.ldb + kk) * 4);
       } else {
         // load l: step l, the lane's NB columns
         const int kk = kstep(l);
-        wv[l] = load_vec<NB>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob,
-                             kk * a.ldb * 4);
+        wv[l] = load_vec<NB, kStream>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob,
+                                      kk * a.ldb * 4);
       }
     }
   };
