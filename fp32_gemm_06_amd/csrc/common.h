@@ -44,13 +44,6 @@ __device__ __forceinline__ float apply_act(float v, int act) {
 // kernels use that to mask rows/columns outside the matrix without branches.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kRsrcRange = 0x7ffffff0;
-// Cache policy of a buffer load (its aux operand) for data read once: the
-// non-temporal bit, so a weight streamed from HBM does not displace what the
-// caches hold for reuse.  The GEMV kernels' weight reads took 1-5% less time
-// with it (M = 1, W stored N x K: 12.9 -> 12.45 us at 4096^2, 31.0 -> 29.5 at
-// N = 11008; stored K x N 36.4 -> 35.7), the skinny kernel's over W stored
-// K x N up to 4% (M = 32, N = 11008: 47.3 -> 45.4 us).
-constexpr int kStream = 2;
 constexpr uint32_t kOob = 0x80000000u;  // an offset the range check rejects
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {

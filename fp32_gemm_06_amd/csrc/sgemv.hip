@@ -97,12 +97,11 @@ sgemv_kernel(GemmArgs a, int transA) {
       const bool ok = col_ok & (k0 + rl + u < K);  // "&": no short circuit, no branch
       const uint32_t off = ok ? (uint32_t)((g * U + u) * a.ldb + cl) * 4u : kOob;
       if constexpr (VEC) {
-        const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream);
+        const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[u][e] = v[e];
       } else {
-        w[u][0] = __builtin_bit_cast(float,
-                                     __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, kStream));
+        w[u][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 0));
       }
     }
   };
@@ -264,12 +263,12 @@ sgemv_rows_kernel(GemmArgs a, int transA) {
         const int k = k0 + p * STEP + li * VW;
         const uint32_t off = (live[r] & (k < K)) ? rowoff[r] + (uint32_t)k * 4u : kOob;
         if constexpr (VEC) {
-          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
+          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[r][p][e] = v[e];
         } else {
-          w[r][p][0] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kStream));
+          w[r][p][0] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
         }
       }
   };

@@ -51,19 +51,18 @@ constexpr int pow2_floor(int v) {
 template <int E> struct Vec { typedef float type __attribute__((ext_vector_type(E))); };
 template <> struct Vec<1> { typedef float type; };
 
-// One raw buffer load of E floats (E = 1, 2, 4) at voffset + soffset bytes,
-// with cache policy AUX.
-template <int E, int AUX = 0>
+// One raw buffer load of E floats (E = 1, 2, 4) at voffset + soffset bytes.
+template <int E>
 __device__ __forceinline__ typename Vec<E>::type load_vec(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                                          int soff) {
   if constexpr (E == 4)
     return __builtin_bit_cast(typename Vec<4>::type,
-                              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, AUX));
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
   else if constexpr (E == 2)
     return __builtin_bit_cast(typename Vec<2>::type,
-                              __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, AUX));
+                              __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
   else
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, AUX));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
 }
 
 template <int E>
@@ -161,15 +160,13 @@ skinny_kernel(GemmArgs a) {
         // WV == 4: K % 4 == 0 and kk + 4 q is a multiple of 4, so the four k
         // are all inside K or all past it
         const int e = l / (WL / NB), kk = kstep(l % (WL / NB) * WV);
-        // (the default cache policy: with the non-temporal bit the halves of
-        // a line read by consecutive loads cost up to 13% at N = 11008)
         wv[l] = load_vec<WV>(rw, r0 + 4 * q + kk < K ? w_lane[e] : kOob,
                              (16 * e * a.ldb + kk) * 4);
       } else {
         // load l: step l, the lane's NB columns
         const int kk = kstep(l);
-        wv[l] = load_vec<NB, kStream>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob,
-                                      kk * a.ldb * 4);
+        wv[l] = load_vec<NB>(rw, (col_ok & (r0 + 4 * q + kk < K)) ? w_off : kOob,
+                             kk * a.ldb * 4);
       }
     }
   };
