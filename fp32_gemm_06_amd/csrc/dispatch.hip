@@ -274,6 +274,15 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
     const int id = find_gemv(mf);
     return id >= 0 ? id : 0;
   }
+  // From M = 5 on, while its stripes fit one round of workgroups, the skinny
+  // MFMA kernel is the faster (4096^2, M = 8: 20.1 us against 22.1 on the
+  // column stripes; 8 x 4096 x 11008: 48.9 against 50.7; at M = 4 they are
+  // 2% apart and at N = 11008 the 64-column stripe is 1.5% ahead).
+  if (M >= 5 && (long long)N * (batch > 1 ? batch : 1) <= 256 * 32) {
+    const int snb = skinny_stripe_blocks(M, N, batch, false);
+    const int id = find_gemv(snb == 4 ? "mfma64_w8" : snb == 2 ? "mfma32_w8" : "mfma16_w8");
+    if (id >= 0) return id;
+  }
   // Wider column stripes read longer runs of each row of W (64, 128 or 256
   // bytes), which the memory system serves faster, but give fewer
   // workgroups.

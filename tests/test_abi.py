@@ -288,12 +288,16 @@ def test_stripe_width_by_rounds():
     per workgroup), within each configuration's row limit."""
     name = lambda *s: fg.fp32gemm_config_name(1, fg.fp32gemm_select_config(1, *s))
     # M <= 8: 16 columns while one round holds the grid (N <= 4096), then 32, then 64
-    assert name(1, 4096, 4096) == "c16_w8_u4"
-    assert name(4, 4096, 4096) == "c16_w4_u8"
+    assert name(1, 4000, 4096) == "c16_w8_u4"
+    assert name(4, 4000, 4096) == "c16_w4_u8"
     for N in (4608, 6144, 7168):
         assert name(1, N, 4096) == "c32_w8_u4", N
     assert name(1, 9216, 4096) == "c64_w8_u4"
     assert name(8, 16384, 4096) == "c64_w8_u4"
+    # M = 5..8 on the skinny kernel while its stripes fit one round
+    assert name(8, 4000, 4096) == "mfma16_w8"
+    assert name(6, 8192, 2048) == "mfma32_w8"
+    assert name(8, 9216, 4096) == "c64_w8_u4"
     # skinny kernel: 64-column stripes up to M = 64, 32-column up to 128
     assert name(16, 4096, 4096) == "mfma16_w8"
     assert name(48, 4608, 4096) == "mfma32_w8"
