@@ -100,7 +100,15 @@ skinny_kernel(GemmArgs a) {
   // accumulator sets: with few independent blocks, consecutive steps
   // alternate between sets so that no MFMA waits on the one before it
   constexpr int NA = MB * NB >= 4 ? 1 : 4 / (MB * NB);
-  constexpr int XBUF = 2 * MR * SK, RED = kSkWaves * MR * CW;
+  // X straight into registers (op(A) = A, float4 loads): each wave multiplies
+  // only its own RW rows of K of a pass, so its X values need no sharing
+  // through LDS and the passes need no barrier.  Taken for one row block over
+  // W stored N x K (4096^2: M = 9 20.0 -> 17.3 us, M = 16 19.9 -> 19.1);
+  // with more blocks the scattered 16-byte X loads cost more than the staging
+  // saves (M = 64: 33.8 -> 38.8 us), and over W stored K x N it was mixed
+  // (M = 16 at 4096^2: 21.4 -> 22.6).
+  constexpr bool XR = !TA && XV && TB && MB == 1;
+  constexpr int XBUF = XR ? 0 : 2 * MR * SK, RED = kSkWaves * MR * CW;
   static_assert(G % 4 == 0, "A fragments are read four steps at a time");
   static_assert(!TA || kSkThreads % MR == 0,
                 "op(A) = A^T stages whole columns of X per thread group");
@@ -243,16 +251,32 @@ skinny_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < NB; ++e) acc[s][j][e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // X in registers: lane (q, c) loads X[16 j + c][k0 + wave RW + 16 t + 4 q
+  // .. + 3] for block j and step group t, the A operand of four steps.
+  typedef floatx4 xq_t[MB][G / 4 > 0 ? G / 4 : 1];
+  const uint32_t xq_lane = ((uint32_t)c * (uint32_t)a.lda + (uint32_t)(4 * q)) * 4u;
+  auto load_xq = [&](xq_t &xv, int k0) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + k0 + wave * RW);
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int t = 0; t < G / 4; ++t) {
+        // K % 4 == 0 here, so a float4 is all inside K or all past it
+        const bool ok = (c + 16 * j < a.M) & (k0 + wave * RW + 16 * t + 4 * q < K);
+        xv[j][t] = load_vec<4>(rx, ok ? xq_lane : kOob, (16 * j * a.lda + 16 * t) * 4);
+      }
+  };
+
   // step g = 4 t + s of this lane: A = X[16 j + c][wave RW + 16 t + 4 q + s],
   // B = element e of the W value of step g
-  auto compute = [&](const wload_t (&wv)[WL], int buf) {
-    const float *xb = &xs[buf * MR * SK + c * SK + wave * RW + 4 * q];
+  auto compute = [&](const wload_t (&wv)[WL], int buf, const xq_t &xv) {
+    const float *xb = &xs[XR ? 0 : buf * MR * SK + c * SK + wave * RW + 4 * q];
 #pragma unroll
     for (int t = 0; t < G / 4; ++t) {
       floatx4 av[MB];
 #pragma unroll
       for (int j = 0; j < MB; ++j)
-        av[j] = *reinterpret_cast<const floatx4 *>(xb + 16 * j * SK + 16 * t);
+        av[j] = XR ? xv[j][t] : *reinterpret_cast<const floatx4 *>(xb + 16 * j * SK + 16 * t);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -276,29 +300,52 @@ skinny_kernel(GemmArgs a) {
   constexpr int D = MB == 1 || (MB == 2 && !TB) ? 2 : MB <= 4 ? 4 : 8;
   static_assert(D % 2 == 0, "pass parity selects the X buffer");
   wload_t wr[D][WL];
-  xvec_t xr[XP];
-  load_x(xr, 0);
+  if constexpr (XR) {
+    // X one pass ahead in two register sets, W D passes deep; no barrier
+    xq_t xq[2];
+    load_xq(xq[0], 0);
 #pragma unroll
-  for (int p = 0; p + 1 < D; ++p) load_w(wr[p], p * ROWS);
-  store_x(xr, 0);
-  __syncthreads();
-  // The scheduling barriers keep each prefetch ahead of the compute that
-  // waits on an earlier pass.  Passes run in groups of D; a pass that starts
-  // past K (only in the last group) skips its multiply, its loads read zeros.
-  for (int k0 = 0; k0 < K; k0 += D * ROWS) {
+    for (int p = 0; p + 1 < D; ++p) load_w(wr[p], p * ROWS);
+    for (int k0 = 0; k0 < K; k0 += D * ROWS) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int kp = k0 + u * ROWS;
-      load_x(xr, kp + ROWS);
-      load_w(wr[(u + D - 1) % D], kp + (D - 1) * ROWS);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (D > 2) {
-        if (kp < K) compute(wr[u], u % 2);
-      } else {
-        compute(wr[u], u % 2);  // at most one pass past K, on zeros
+      for (int u = 0; u < D; ++u) {
+        const int kp = k0 + u * ROWS;
+        load_xq(xq[(u + 1) % 2], kp + ROWS);
+        load_w(wr[(u + D - 1) % D], kp + (D - 1) * ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (D > 2) {
+          if (kp < K) compute(wr[u], 0, xq[u % 2]);
+        } else {
+          compute(wr[u], 0, xq[u % 2]);  // at most one pass past K, on zeros
+        }
       }
-      store_x(xr, (u + 1) % 2);
-      __syncthreads();
+    }
+  } else {
+    xvec_t xr[XP];
+    xq_t none;
+    load_x(xr, 0);
+#pragma unroll
+    for (int p = 0; p + 1 < D; ++p) load_w(wr[p], p * ROWS);
+    store_x(xr, 0);
+    __syncthreads();
+    // The scheduling barriers keep each prefetch ahead of the compute that
+    // waits on an earlier pass.  Passes run in groups of D; a pass that starts
+    // past K (only in the last group) skips its multiply, its loads read zeros.
+    for (int k0 = 0; k0 < K; k0 += D * ROWS) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int kp = k0 + u * ROWS;
+        load_x(xr, kp + ROWS);
+        load_w(wr[(u + D - 1) % D], kp + (D - 1) * ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (D > 2) {
+          if (kp < K) compute(wr[u], u % 2, none);
+        } else {
+          compute(wr[u], u % 2, none);  // at most one pass past K, on zeros
+        }
+        store_x(xr, (u + 1) % 2);
+        __syncthreads();
+      }
     }
   }
 
