@@ -103,11 +103,13 @@ skinny_kernel(GemmArgs a) {
   // X straight into registers (op(A) = A, float4 loads): each wave multiplies
   // only its own RW rows of K of a pass, so its X values need no sharing
   // through LDS and the passes need no barrier.  Taken for one row block over
-  // W stored N x K (4096^2: M = 9 20.0 -> 17.3 us, M = 16 19.9 -> 19.1);
+  // W stored N x K (4096^2: M = 9 20.0 -> 17.3 us, M = 16 19.9 -> 19.1) and
+  // on 64-column stripes over W stored K x N (N = 11008, M = 9: 41.8 -> 38.8);
   // with more blocks the scattered 16-byte X loads cost more than the staging
-  // saves (M = 64: 33.8 -> 38.8 us), and over W stored K x N it was mixed
-  // (M = 16 at 4096^2: 21.4 -> 22.6).
-  constexpr bool XR = !TA && XV && TB && MB == 1;
+  // saves (M = 64: 33.8 -> 38.8 us), and on narrower stripes over W stored
+  // K x N it was mixed (M = 16 at 4096^2: 21.4 -> 22.6; at 8192^2 27.3 ->
+  // 28.4).
+  constexpr bool XR = !TA && XV && MB == 1 && (TB || NB == 4);
   constexpr int XBUF = XR ? 0 : 2 * MR * SK, RED = kSkWaves * MR * CW;
   static_assert(G % 4 == 0, "A fragments are read four steps at a time");
   static_assert(!TA || kSkThreads % MR == 0,
