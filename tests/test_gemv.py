@@ -174,3 +174,17 @@ def test_wide_rows_batched_wide_stripes(tb, M, offset):
     for b in range(4):
         assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5),
                         f"M={M} tb={tb} offset={offset} entry {b}")
+
+
+@pytest.mark.parametrize("tb,M,N", [(1, 9, 530), (1, 12, 4096), (1, 16, 1000), (0, 9, 12288),
+                                    (0, 16, 12288)])
+def test_one_row_block_x_in_registers(tb, M, N):
+    """One row block with op(A) = A on aligned rows: over W stored N x K, and on
+    64-column stripes over W stored K x N, the skinny kernel loads X straight
+    into registers (no LDS staging, no per-pass barrier).  K = 1028 ends in a
+    partial pass; rows past M and k past K read zeros."""
+    from test_transpose_batched import _case, run_batched
+    As, Bs, Cs = _case(7600 + M + N + tb, M, N, 1028)
+    (got,), ok = run_batched(0, tb, As, Bs, Cs, 1.0, 0.5)
+    assert ok, "write outside C"
+    assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5), f"M={M} N={N} tb={tb}")
