@@ -25,11 +25,15 @@
 //    each of 16 consecutive rows;
 //  * X is staged per pass in LDS as [m][k] rows with a stride of ROWS + 8
 //    floats; one ds_read_b128 holds the A operand of four consecutive steps.
+//    With one row block (and 16-byte aligned rows) a wave can instead load
+//    its own part of X straight into registers, which needs no LDS and no
+//    barrier between passes (see XR below).
 //    With a stride of ROWS + 4 the counters showed about two bank-conflict
 //    cycles per LDS instruction, with ROWS + 8 one in seventeen (ROWS + 16
 //    and + 20 as many as + 4); the time did not change;
 //  * M up to 16 MB rows, MB blocks of 16 sharing each W value; W runs D
-//    passes deep in registers and X one pass ahead through two LDS buffers,
+//    passes deep in registers and X one pass ahead (two LDS buffers or two
+//    register sets),
 //    with the same branch-free masking as the GEMV: rows of X past M and
 //    rows of W past K (or N) read zeros through an out-of-range buffer offset;
 //  * the waves' partial sums are added in LDS in wave order: the result does
