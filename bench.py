@@ -270,13 +270,18 @@ def main():
         oracle.sgemm(A[:r0], B, None, 1.0, 0.0)
         t_cal = time.perf_counter() - t0
         rows = int(min(M, max(r0, r0 * args.cpu_seconds / max(t_cal, 1e-6))))
-        t0 = time.perf_counter()
-        oracle.sgemm(A[:rows], B, None, 1.0, 0.0)
-        t = time.perf_counter() - t0
-        cpu = {"value": round(acc.flops(rows, N, K) / t / 1e12, 6), "unit": "TFLOP/s",
+        # whole passes until the target CPU time is reached (the full product
+        # can take less than the target)
+        passes, t = 0, 0.0
+        while passes == 0 or (t < args.cpu_seconds and passes < 20):
+            t0 = time.perf_counter()
+            oracle.sgemm(A[:rows], B, None, 1.0, 0.0)
+            t += time.perf_counter() - t0
+            passes += 1
+        cpu = {"value": round(passes * acc.flops(rows, N, K) / t / 1e12, 6), "unit": "TFLOP/s",
                "cores": cores, "kind": "oracle",
                "sample": f"first {rows} of {M} rows of the 4092^3 product (fp64 triple loop), "
-                         f"{t:.2f} s"}
+                         f"{passes} pass(es), {t:.2f} s"}
 
     traffic = stored_traffic("sgemm_4092", KERNEL_SOURCES)
     out = {
