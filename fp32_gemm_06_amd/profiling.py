@@ -7,6 +7,11 @@ counter runs (pmc*/), each made with ``--output-format csv``.  Writes
 <out prefix>_<kernel>.md summaries and, for the SGEMM and the two GEMV kernels,
 <out prefix>_<kernel>_traffic.json with HBM bytes per launch.
 
+    python -m fp32_gemm_06_amd.profiling --trace-table <run dir> <out.md> "<command>"
+
+writes one table of this library's launches in a kernel-trace run, by kernel
+and launch shape (calls, mean and min duration).
+
 HBM bytes come from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
 scaled by what the same counter reads for a calibration kernel of known
 size in the same run (an elementwise negation that reads and writes
@@ -167,6 +172,57 @@ def summarize(run_dir, prefix, command, timed=(100, 400)):
     return written
 
 
+def _short_kernel(name):
+    """This library's kernel name without namespaces and parameter list."""
+    name = name.replace("void ", "", 1).replace("fp32gemm::(anonymous namespace)::", "")
+    name = name.replace("fp32gemm::", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def trace_table(run_dir, out_md, command):
+    """Per-launch-shape durations of this library's kernels from a
+    `rocprofv3 --kernel-trace` run: one row per (kernel, workgroups,
+    workgroup size) with calls, mean and min duration."""
+    hits = sorted(glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no kernel_trace.csv under {run_dir}")
+    groups, other = {}, 0
+    with open(hits[0], newline="") as f:
+        for r in csv.DictReader(f):
+            if "fp32gemm::" not in r["Kernel_Name"]:
+                other += 1
+                continue
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                    int(r["Grid_Size_Y"]) // max(1, int(r["Workgroup_Size_Y"])))
+            key = (_short_kernel(r["Kernel_Name"]), grid, wg)
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(d)
+    lines = [f"# Kernel trace: {os.path.basename(out_md)[:-3]}", "",
+             "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
+             "One row per kernel and launch shape (workgroups x batch entries, threads per "
+             "workgroup); durations in microseconds from the kernel trace. "
+             f"{other} dispatches of other kernels (input generation, the vendor library) "
+             "are not listed.", "",
+             "| kernel | workgroups | threads | calls | mean us | min us |",
+             "|---|---|---|---|---|---|"]
+    for (k, grid, wg), v in sorted(groups.items()):
+        lines.append(f"| `{k}` | {grid[0]} x {grid[1]} | {wg} | {len(v)} | "
+                     f"{sum(v) / len(v):.1f} | {min(v):.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_md
+
+
 if __name__ == "__main__":
-    for w in summarize(sys.argv[1], sys.argv[2], sys.argv[3]):
-        print(w)
+    if sys.argv[1] == "--trace-table":
+        print(trace_table(sys.argv[2], sys.argv[3], sys.argv[4]))
+    else:
+        for w in summarize(sys.argv[1], sys.argv[2], sys.argv[3]):
+            print(w)
