@@ -125,7 +125,8 @@ def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
 
 
 def sgemv(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
-    """Same operation for 1 <= M <= 8 (decode shape); returns the C return code."""
+    """Same operation for 1 <= M <= 128 (decode shapes: GEMV kernels up to
+    M = 8, the skinny MFMA kernel above); returns the C return code."""
     return lib().sgemv(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                        _stream(stream))
 

@@ -195,9 +195,16 @@ int fp32gemm_splitk_splits(int M, int N, int K);
 const char *fp32gemm_strerror(int code);
 
 /*
- * Tuning and testing hooks.  kind 0 = the SGEMM kernel family, kind 1 = the
- * GEMV family.  Configurations are numbered 0 .. fp32gemm_num_configs(kind)-1
- * and named by fp32gemm_config_name (NULL for an unknown id).
+ * Tuning and testing hooks.  These expose the per-shape parameter search of
+ * "CUDA 矩阵乘法优化：从朴素 Kernel 到接近 cuBLAS", section "8. Kernel 9:
+ * 参数自动调优": the tile parameters (block tile, K depth, wave tile) are
+ * enumerated, each candidate is timed on the target GPU, and the fastest per
+ * shape goes into a table, because the best choice differs between GPUs.
+ * The tuner (fp32_gemm_06_amd/tune.py) drives the sweep through these calls.
+ * kind 0 = the SGEMM kernel family, kind 1 = the GEMV family.
+ * Configurations are numbered 0 .. fp32gemm_num_configs(kind)-1 and named by
+ * fp32gemm_config_name (NULL for an unknown id); an unknown kind gives 0
+ * configurations, NULL names and FP32GEMM_ERR_CONFIG selections.
  */
 int fp32gemm_num_configs(int kind);
 const char *fp32gemm_config_name(int kind, int cfg);

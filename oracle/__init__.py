@@ -233,17 +233,25 @@ def threads(lib=None) -> int:
 
 
 def within_tolerance(got, ref, bnd, rel: float = 1e-4):
-    """Acceptance rule: |got - ref| <= rel * bnd on every element, and no
-    NaN/Inf in `got` unless `ref` has one there.  Returns (ok, worst ratio)."""
+    """Acceptance rule: |got - ref| <= rel * bnd on every element where the
+    reference is finite (and got must be finite there too); where the
+    reference is NaN, got must be NaN, and where it is +-Inf, got must be the
+    same infinity.  Returns (ok, worst ratio over the finite elements)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     bnd = np.asarray(bnd, dtype=np.float64)
     finite_ref = np.isfinite(ref)
     bad_nonfinite = ~np.isfinite(got) & finite_ref
-    err = np.abs(got - ref)
+    # non-finite reference values are matched exactly: NaN by NaN, an
+    # infinity by the same-signed infinity
+    nan_ref = np.isnan(ref)
+    inf_ref = np.isinf(ref)
+    bad_nan = nan_ref & ~np.isnan(got)
+    bad_inf = inf_ref & (got != ref)
     with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.abs(got - ref)
         ratio = np.where(bnd > 0, err / (rel * bnd), np.where(err == 0, 0.0, np.inf))
     ratio = np.where(finite_ref, ratio, 0.0)
     worst = float(ratio.max()) if ratio.size else 0.0
-    ok = (not bad_nonfinite.any()) and worst <= 1.0
+    ok = not (bad_nonfinite.any() or bad_nan.any() or bad_inf.any()) and worst <= 1.0
     return ok, worst

@@ -35,9 +35,27 @@ def test_within_tolerance_rule():
     import numpy as np
     ref = np.array([1.0, 2.0, np.nan])
     bnd = np.array([1.0, 1.0, 1.0])
-    ok, worst = oracle.within_tolerance(np.array([1.0 + 5e-5, 2.0, 3.0]), ref, bnd)
+    ok, worst = oracle.within_tolerance(np.array([1.0 + 5e-5, 2.0, np.nan]), ref, bnd)
     assert ok and worst == pytest.approx(0.5)
-    ok, _ = oracle.within_tolerance(np.array([1.0 + 2e-4, 2.0, 0.0]), ref, bnd)
+    ok, _ = oracle.within_tolerance(np.array([1.0 + 2e-4, 2.0, np.nan]), ref, bnd)
     assert not ok
-    ok, _ = oracle.within_tolerance(np.array([1.0, np.inf, 0.0]), ref, bnd)
+    ok, _ = oracle.within_tolerance(np.array([1.0, np.inf, np.nan]), ref, bnd)
     assert not ok
+
+
+def test_within_tolerance_matches_non_finite_reference():
+    """Where the reference is NaN or +-Inf, the result must be the same
+    non-finite value: a finite value, a NaN for an infinity, or an infinity
+    of the other sign all fail."""
+    import numpy as np
+    ref = np.array([np.nan, np.inf, -np.inf, 3.0])
+    bnd = np.array([1.0, 1.0, 1.0, 1.0])
+    ok, worst = oracle.within_tolerance(np.array([np.nan, np.inf, -np.inf, 3.0]), ref, bnd)
+    assert ok and worst == 0.0
+    for bad in ([0.0, np.inf, -np.inf, 3.0],       # NaN turned finite
+                [np.nan, 1e30, -np.inf, 3.0],      # +Inf turned finite
+                [np.nan, -np.inf, -np.inf, 3.0],   # +Inf of the wrong sign
+                [np.nan, np.inf, np.nan, 3.0],     # -Inf turned NaN
+                [np.inf, np.inf, -np.inf, 3.0]):   # NaN turned Inf
+        ok, _ = oracle.within_tolerance(np.array(bad), ref, bnd)
+        assert not ok, bad
