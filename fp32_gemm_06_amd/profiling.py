@@ -12,6 +12,12 @@ counter runs (pmc*/), each made with ``--output-format csv``.  Writes
 writes one table of this library's launches in a kernel-trace run, by kernel
 and launch shape (calls, mean and min duration).
 
+    python -m fp32_gemm_06_amd.profiling --workload <run dir> <tag> <kernel needle>
+        <skip> <count> <per step> <source files> <out dir> "<command>"
+
+summarizes one workload's timed calls from a run that launched only that
+workload (``bench.py --only <workload>``): see ``summarize_workload``.
+
 HBM bytes come from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
 scaled by what the same counter reads for a calibration kernel of known
 size in the same run (an elementwise negation that reads and writes
@@ -172,6 +178,96 @@ def summarize(run_dir, prefix, command, timed=(100, 400)):
     return written
 
 
+def summarize_workload(run_dir, tag, needle, skip, count, per_step, sources, out_dir, command):
+    """Summary of one workload's timed calls in a run that launched only that
+    workload's products (``bench.py --only``).
+
+    The dispatches whose kernel name contains ``needle`` are taken in launch
+    order; the timed window is ``count`` of them after the first ``skip``
+    (parity call and warm-up).  A call of the workload is ``per_step``
+    consecutive dispatches (two for a product that runs as two launches), and
+    its duration is their sum.  Counters from the pmc*/ runs are averaged per
+    kernel over all its dispatches and summed over the kernels of one call.
+    Writes ``rocprof_<tag>.md`` and, when both byte counters and the
+    calibration kernel are present, ``<tag>_traffic.json``.
+    """
+    hits = sorted(glob.glob(os.path.join(run_dir, "trace", "*kernel_trace.csv")))
+    if not hits:
+        raise FileNotFoundError(f"no kernel_trace.csv under {run_dir}/trace")
+    rows = []
+    for path in hits:
+        rows += [r for r in csv.DictReader(open(path)) if needle in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    win = rows[skip: skip + count]
+    if len(win) < count or count % per_step:
+        raise ValueError(f"{tag}: {len(rows)} dispatches of {needle!r}, window {skip}+{count} "
+                         f"in calls of {per_step}")
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in win]
+    calls = [sum(durs[i:i + per_step]) for i in range(0, len(durs), per_step)]
+    names = []
+    for r in win[:per_step]:
+        if r["Kernel_Name"] not in names:
+            names.append(r["Kernel_Name"])
+    per_kernel = {}
+    for k in names:
+        d = [x for x, r in zip(durs, win) if r["Kernel_Name"] == k]
+        grid = (int(win[[r["Kernel_Name"] for r in win].index(k)]["Grid_Size_X"]))
+        per_kernel[k] = (sum(d) / len(d), grid)
+    ctr = counters(run_dir)
+    calib = _find(ctr, CALIB)
+    scales = {}
+    if calib:
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            if ctr[calib].get(cn):
+                scales[cn] = CALIB_BYTES / (max(ctr[calib][cn]) * 1024.0)
+    summed = defaultdict(float)
+    for k in names:
+        for cn, vals in ctr.get(k, {}).items():
+            summed[cn] += _avg(vals)
+    h = source_hash(sources)
+    avg_call = sum(calls) / len(calls)
+    lines = [f"# {tag}: rocprofv3 summary", "",
+             "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
+             f"Kernel source hash: `{h}`", "",
+             f"One call = {per_step} dispatch(es); timed window: {len(calls)} calls after "
+             f"{skip} earlier dispatches (parity call and warm-up).", "",
+             "| kernel | grid threads (x) | mean duration in the window |", "|---|---|---|"]
+    for k in names:
+        lines.append(f"| `{_short_kernel(k)}` | {per_kernel[k][1]} | {per_kernel[k][0]:.3f} us |")
+    lines += ["", "| quantity | value |", "|---|---|",
+              f"| calls in the window | {len(calls)} |",
+              f"| mean duration per call (sum of its dispatches) | {avg_call:.3f} us |",
+              f"| min / max per call | {min(calls):.3f} / {max(calls):.3f} us |"]
+    rec = {"workload": tag, "kernels": names, "source_hash": h, "per_step": per_step,
+           "timed_avg_us": avg_call}
+    for cn in sorted(summed):
+        lines.append(f"| {cn} (mean per call, summed over its kernels) | {summed[cn]:.6g} |")
+    if summed.get("SQ_VALU_MFMA_BUSY_CYCLES") and summed.get("GRBM_GUI_ACTIVE"):
+        util = summed["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / (summed["GRBM_GUI_ACTIVE"] / 8.0)
+        lines.append(f"| MFMA busy fraction (busy per SIMD / active cycles per XCD) | {util:.4f} |")
+        rec["mfma_busy_fraction"] = util
+    for cn, key in (("FETCH_SIZE", "fetch_bytes"), ("WRITE_SIZE", "write_bytes")):
+        if summed.get(cn) and cn in scales:
+            b = summed[cn] * 1024.0 * scales[cn]
+            lines.append(f"| HBM {'read' if cn == 'FETCH_SIZE' else 'write'} bytes per call "
+                         f"({cn} x {scales[cn]:.4f}) | {b:.6g} |")
+            rec[key] = b
+            rec[key.replace("bytes", "scale")] = scales[cn]
+    if "fetch_bytes" in rec and "write_bytes" in rec:
+        rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    if calib:
+        lines += ["", f"Calibration kernel `{_short_kernel(calib)[:60]}` moves {CALIB_BYTES} bytes "
+                      "each way; counter scale = known bytes / counted bytes."]
+    out = [os.path.join(out_dir, f"rocprof_{tag}.md")]
+    with open(out[0], "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if "bytes_per_launch" in rec:
+        out.append(os.path.join(out_dir, f"{tag}_traffic.json"))
+        with open(out[1], "w") as f:
+            json.dump(rec, f, indent=1)
+    return out
+
+
 def _short_kernel(name):
     """This library's kernel name without namespaces and parameter list."""
     name = name.replace("void ", "", 1).replace("fp32gemm::(anonymous namespace)::", "")
@@ -221,7 +317,14 @@ def trace_table(run_dir, out_md, command):
 
 
 if __name__ == "__main__":
-    if sys.argv[1] == "--trace-table":
+    if sys.argv[1] == "--workload":
+        # --workload <run dir> <tag> <kernel needle> <skip> <count> <per step>
+        #            <source files, comma-separated> <out dir> "<command>"
+        a = sys.argv[2:]
+        for w in summarize_workload(a[0], a[1], a[2], int(a[3]), int(a[4]), int(a[5]),
+                                    a[6].split(","), a[7], a[8]):
+            print(w)
+    elif sys.argv[1] == "--trace-table":
         print(trace_table(sys.argv[2], sys.argv[3], sys.argv[4]))
     else:
         for w in summarize(sys.argv[1], sys.argv[2], sys.argv[3]):

@@ -62,6 +62,8 @@ def _bind(lib):
                                     _F64P]
     lib.oracle_epilogue.restype = None
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = ctypes.c_int
     return lib
 
 
@@ -230,6 +232,11 @@ def bound_fused_entries(rows, cols, A, B, C0=None, alpha: float = 1.0, beta: flo
 def threads(lib=None) -> int:
     """OpenMP threads the oracle's loops use."""
     return int((lib or load()).oracle_threads())
+
+
+def set_threads(n: int, lib=None) -> int:
+    """Use n OpenMP threads from now on; returns the number in effect."""
+    return int((lib or load()).oracle_set_threads(int(n)))
 
 
 def within_tolerance(got, ref, bnd, rel: float = 1e-4):

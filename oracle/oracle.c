@@ -237,3 +237,14 @@ int oracle_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads the loops above use (n >= 1) and
+ * returns the number in effect afterwards; for timing the oracle on fewer
+ * cores than the host has. */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#endif
+  return oracle_threads();
+}
