@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
 SOURCES = ["api.hip", "dispatch.hip", "sgemm_configs.hip", "sgemm_nn.hip", "sgemm_nt.hip",
-           "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip", "skinny.hip", "splitk.hip"]
+           "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip", "gemv_split.hip", "skinny.hip",
+           "splitk.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

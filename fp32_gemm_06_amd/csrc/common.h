@@ -126,6 +126,16 @@ hipError_t launch_skinny_tb(const GemmArgs &a, int transA, hipStream_t s);
 int skinny_stripe_blocks(int M, int N, int batch, bool transposed_w);
 int gemv_stripe_blocks(int N, int batch);
 
+// Small-M product with W stored K x N, K split across workgroups
+// (gemv_split.hip): 256-column blocks x K chunks, the chunks' partial sums
+// added in chunk order inside the same kernel.  gemv_split_pays: whether the
+// dispatcher takes it for this shape (one product, M <= 8).  The
+// _serial form walks the chunks in one workgroup per column block and needs
+// no scratch; its results are bit-identical.
+bool gemv_split_pays(int M, int N, int K, int batch);
+hipError_t launch_gemv_split(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_gemv_split_serial(const GemmArgs &a, int transA, hipStream_t s);
+
 // Small-M product with op(B) = B^T (B stored N x K): row-dot kernel.
 // rows_per_wave is 1 or 2; <= 0 picks from M.
 hipError_t launch_gemv_rows(const GemmArgs &a, int transA, int rows_per_wave, hipStream_t s);

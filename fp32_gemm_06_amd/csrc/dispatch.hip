@@ -265,7 +265,6 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
         const int id = find_gemv(e.name);
         if (id >= 0) return id;
       }
-  (void)K;
   if (M > 8) {
     // The skinny MFMA kernel (N = 11008, M = 16: 42.1 us on 64 columns
     // against 62.7 on 16; N = 4608, M = 48: 39.7 on 32 against 56.5 on 16).
@@ -273,6 +272,12 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
     const char *mf = nb == 4 ? "mfma64_w8" : nb == 2 ? "mfma32_w8" : "mfma16_w8";
     const int id = find_gemv(mf);
     return id >= 0 ? id : 0;
+  }
+  // W of 16 M floats and more with few column blocks: K split across
+  // workgroups in 1 KB runs of each row (gemv_split.hip).
+  if (gemv_split_pays(M, N, K, batch)) {
+    const int id = find_gemv("split256_w8_u4");
+    if (id >= 0) return id;
   }
   // From M = 5 on, while its stripes fit one round of workgroups, the skinny
   // MFMA kernel is the faster (4096^2, M = 8: 20.1 us against 22.1 on the

@@ -1,0 +1,387 @@
+// Small-M product Y[M x N] <- alpha X[M x K] W[K x N] + beta Y, 1 <= M <= 8,
+// with K split across workgroups and the partial sums added inside the same
+// kernel.
+//
+// This is the decode shape of "GPU GEMM 优化完全拆解（一）", section "LLM 推理
+// 本质上是 GEMM 的串联": the time is the time to stream W once from HBM.  With
+// W stored K x N, a workgroup that owns a column block over all of K reads a
+// short piece of every row (64 bytes for 16 columns at N = 4096, which gives
+// the 256 workgroups that fill the GPU); the memory system serves such
+// pieces far slower than long runs.  Here a workgroup owns 256 columns (one
+// 1 KB run of a row per wave instruction) over a chunk of K, so N = 4096
+// still gives 16 column blocks x 16 chunks = 256 workgroups.  The chunks'
+// partial sums are added in a fixed order by the last workgroup of each
+// column block to finish, in the same kernel: the K split with a reduction
+// step of "CUDA 矩阵乘法优化：从朴素 Kernel 到接近 cuBLAS", section "10. cuBLAS
+// 领先的性能差异", without the second launch.
+//
+// Cross-workgroup protocol (no spin-wait; every workgroup runs to the end):
+//  1. each workgroup writes its partial sums with agent-scope atomic stores,
+//     which the compiler emits as stores with the sc1 bit: they write
+//     through the XCD's L2, so they are visible to every XCD once complete;
+//  2. it waits for its own stores to complete (s_waitcnt vmcnt(0)), then one
+//     thread adds 1 to the column block's counter (agent-scope atomic add);
+//  3. the workgroup that reads count - 1 is the last: its loads of the
+//     partials are agent-scope atomic loads (sc1), which do not return stale
+//     copies from its own L2.  It adds chunk 0, 1, 2, ... in that order,
+//     applies alpha, beta, the bias and the activation, stores Y and puts
+//     the counter back to 0 for the next call.
+// An agent-scope release fence would also write back every dirty line of
+// the XCD's L2 (buffer_wbl2) and an acquire fence would invalidate it
+// (buffer_inv); both serialise per workgroup and cost far more than the
+// whole product.  They are not needed here: every value published across
+// workgroups is written and read by agent-scope atomics, and the wait in
+// step 2 orders their completion before the counter update.
+//
+// Scratch: partial sums and counters live in file-scope device arrays, in
+// slots; each stream gets its own slot on first use (8 per device), so
+// calls on one stream reuse it in stream order and calls on different
+// streams never share one.  With every slot taken, the same kernel runs
+// with one workgroup per column block that walks the chunks itself and adds
+// their partial sums in the same order: bit-identical results, no scratch.
+// Either way the summation order depends only on the shape, never on timing.
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace fp32gemm {
+namespace {
+
+constexpr int kSplitCW = 256;          // columns per workgroup (64 lanes x float4)
+constexpr int kSplitMaxRowsM = 8;      // largest M
+constexpr int kSplitMaxGroups = 256;   // column blocks x chunks per call with scratch
+constexpr int kSplitSlots = 8;         // streams per device with their own scratch
+constexpr int kSplitKcMax = 1024;      // rows of K per chunk (X chunk staged in LDS)
+
+// Partial sums: [column block][chunk][row m][column], MR rows per call.
+__device__ __attribute__((aligned(256)))
+float g_split_partials[kSplitSlots][(size_t)kSplitMaxGroups * kSplitMaxRowsM * kSplitCW];
+// Arrival counters, one per column block; zero between calls.
+__device__ __attribute__((aligned(256))) unsigned g_split_counters[kSplitSlots][kSplitMaxGroups] =
+    {};
+
+// Stream -> slot, per device.  Slots are never released: a stream keeps its
+// slot for the life of the process.
+std::mutex g_slot_mu;
+struct SlotOwner {
+  int dev;
+  hipStream_t stream;
+};
+std::vector<SlotOwner> g_slot_owners;
+
+int split_slot(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lk(g_slot_mu);
+  int used = 0;
+  for (const SlotOwner &o : g_slot_owners) {
+    if (o.dev != dev) continue;
+    if (o.stream == s) return used;
+    ++used;
+  }
+  if (used >= kSplitSlots) return -1;
+  g_slot_owners.push_back({dev, s});
+  return used;
+}
+
+// Workgroup (column block cb, chunk s): rows [s KC, (s + 1) KC) of K, 256
+// columns.  Wave w of a pass takes U consecutive rows, each wave instruction
+// one 1 KB run of a row (lane l: columns 4 l .. 4 l + 3).  D passes of
+// loads are in flight while one is multiplied.  Workgroup ids run over the
+// chunks of one column block first; the hardware deals consecutive ids to
+// the 8 XCDs in turn, so each XCD streams whole rows of its chunks (timed
+// at 4096 x 4096, M = 1, against consecutive column blocks of one chunk:
+// 16.4 against 17.3 us).
+template <int MR, bool VEC, int NW, int U, int D, bool SERIAL>
+__global__ void __launch_bounds__(NW * 64)
+gemv_split_kernel(GemmArgs a, int transA, int S, int KC, int slot) {
+  constexpr int CW = kSplitCW;
+  constexpr int THREADS = NW * 64;
+  constexpr int ROWS = NW * U;                 // rows of W per pass
+  constexpr int OUTS = MR * CW;                // outputs of a column block
+  constexpr int OPT = (OUTS + THREADS - 1) / THREADS;  // outputs per thread
+  constexpr int XS = MR * kSplitKcMax;         // X chunk
+  constexpr int XPT = (XS + THREADS - 1) / THREADS;    // X values staged per thread
+  constexpr int RS = NW * MR * CW;             // per-wave sums
+  static_assert(U % 4 == 0, "X is read in float4 pieces");
+  __shared__ __attribute__((aligned(16))) float smem[XS > RS ? XS : RS];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = a.N, K = a.K;
+  const int id = blockIdx.x;
+  const int cb = SERIAL ? id : id / S;
+  const int s_first = SERIAL ? 0 : id % S;
+  const int s_end = SERIAL ? S : s_first + 1;
+  const int n0 = cb * CW;
+  const int c0 = 4 * lane;                     // first column of this lane in the block
+  // X element (m, k) sits at A + k * xk + m * xm
+  const uint32_t xk = transA ? (uint32_t)a.lda : 1u, xm = transA ? 1u : (uint32_t)a.lda;
+  const float alpha = a.alpha, beta = a.beta;
+
+  float total[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) total[j] = 0.0f;
+
+  for (int s = s_first; s < s_end; ++s) {
+    const int k0 = s * KC;
+    const int kend = min(K, k0 + KC);
+
+    // rows k0 + r0 + wave * U + u of this lane's four columns (zeros past
+    // the chunk); the wave's first row goes into the buffer base so byte
+    // offsets stay small
+    auto load_w = [&](float (&w)[U][4], int r0) {
+      const int rw = k0 + r0 + wave * U;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B + (size_t)rw * a.ldb + n0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool row_ok = rw + u < kend;
+        if constexpr (VEC) {
+          const uint32_t off = (row_ok & (n0 + c0 < N)) ? (uint32_t)(u * a.ldb + c0) * 4u : kOob;
+          const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[u][e] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t off =
+                (row_ok & (n0 + c0 + e < N)) ? (uint32_t)(u * a.ldb + c0 + e) * 4u : kOob;
+            w[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+          }
+        }
+      }
+    };
+
+    // X(m, k0 .. k0 + KC) as [m][kk] (zeros past the chunk): its loads go
+    // out first, then the first D passes of W, so the two latencies overlap
+    float xr[XPT];
+    {
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.A + (size_t)k0 * xk);
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int i = tid + j * THREADS, m = i / KC, kk = i - m * KC;
+        const bool ok = (i < MR * KC) & (k0 + kk < kend);
+        const uint32_t off = ok ? ((uint32_t)kk * xk + (uint32_t)m * xm) * 4u : kOob;
+        xr[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+      }
+    }
+    float w[D][U][4];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(w[d], d * ROWS);
+    __syncthreads();  // the previous chunk's sums have been read (SERIAL)
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + j * THREADS;
+      if (i < MR * KC) smem[i] = xr[j];
+    }
+    __syncthreads();
+
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[m][e] = 0.0f;
+    // every lane of a wave uses the same rows, so the X reads are broadcasts
+    auto multiply = [&](const float (&wv)[U][4], int r0) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int q = 0; q < U / 4; ++q) {
+          const floatx4 xv =
+              *reinterpret_cast<const floatx4 *>(&smem[m * KC + r0 + wave * U + 4 * q]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m][e] += xv[t] * wv[4 * q + t][e];
+        }
+    };
+    // KC is a multiple of D passes; each multiply frees its registers for
+    // the pass D ahead (past the chunk: out-of-range offsets, no traffic)
+    for (int r0 = 0; r0 < KC; r0 += D * ROWS) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        multiply(w[d], r0 + d * ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[d], r0 + (d + D) * ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // per-wave sums into LDS (the X chunk is no longer read), then the waves
+    // in wave order
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      *reinterpret_cast<floatx4 *>(&smem[(wave * MR + m) * CW + c0]) =
+          floatx4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int o = tid + j * THREADS;
+      if (OUTS % THREADS == 0 || o < OUTS) {
+        float p = smem[o];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) p += smem[w2 * OUTS + o];
+        if constexpr (SERIAL) {
+          total[j] = (s == 0) ? p : total[j] + p;
+        } else {
+          float *ws = &g_split_partials[slot][((size_t)cb * S + s) * OUTS];
+          __hip_atomic_store(&ws[o], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+
+  if constexpr (!SERIAL) {
+    // publish: this workgroup's partial sums have completed, then count it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned before = __hip_atomic_fetch_add(&g_split_counters[slot][cb], 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = before == (unsigned)(S - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    asm volatile("" ::: "memory");
+    const float *ws = &g_split_partials[slot][(size_t)cb * S * OUTS];
+    // chunks in order; the loads of a group are issued together, so a group
+    // costs one memory round trip
+    constexpr int G = 16;
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int o = tid + j * THREADS;
+      if ((OUTS % THREADS == 0 || o < OUTS) && n0 + o % CW < N) {
+        float t = 0.0f;
+        for (int s0 = 0; s0 < S; s0 += G) {
+          float v[G];
+#pragma unroll
+          for (int i = 0; i < G; ++i)
+            v[i] = s0 + i < S ? __hip_atomic_load(&ws[(size_t)(s0 + i) * OUTS + o],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.0f;
+#pragma unroll
+          for (int i = 0; i < G; ++i)
+            if (s0 + i < S) t = s0 + i == 0 ? v[i] : t + v[i];
+        }
+        total[j] = t;
+      }
+    }
+    if (tid == 0)
+      __hip_atomic_store(&g_split_counters[slot][cb], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // alpha / beta update, bias and activation
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int o = tid + j * THREADS;
+    const int m = o / CW, n = n0 + o % CW;
+    if ((OUTS % THREADS == 0 || o < OUTS) && n < N) {
+      float *y = a.C + (size_t)m * a.ldc + n;
+      float out = alpha * total[j];
+      if (beta != 0.0f) out += beta * *y;
+      if (a.bias) out += a.bias[n];
+      *y = apply_act(out, a.act);
+    }
+  }
+}
+
+// Chunking for a shape: about `target` workgroups, chunks a multiple of
+// `step` rows (whole groups of D passes) and at most kSplitKcMax.
+struct SplitPlan {
+  int ncb, S, KC;
+};
+
+SplitPlan split_plan(int N, int K, int target, int step) {
+  SplitPlan p;
+  p.ncb = (N + kSplitCW - 1) / kSplitCW;
+  int s = target / p.ncb;
+  if (s < 1) s = 1;
+  int kc = (K + s - 1) / s;
+  kc = (kc + step - 1) / step * step;
+  const int kc_max = kSplitKcMax / step * step;
+  if (kc > kc_max) kc = kc_max;
+  p.KC = kc;
+  p.S = (K + kc - 1) / kc;
+  return p;
+}
+
+template <bool VEC, int NW, int U, int D, bool SERIAL>
+hipError_t launch_split_m(const GemmArgs &a, int transA, const SplitPlan &p, int slot,
+                          hipStream_t s) {
+  const dim3 grid((unsigned)(SERIAL ? p.ncb : p.ncb * p.S)), block(NW * 64);
+  switch (a.M) {
+#define FP32GEMM_SPLIT_CASE(MR)                                                               \
+  case MR:                                                                                    \
+    hipLaunchKernelGGL((gemv_split_kernel<MR, VEC, NW, U, D, SERIAL>), grid, block, 0, s, a,  \
+                       transA, p.S, p.KC, slot);                                              \
+    break;
+    FP32GEMM_SPLIT_CASE(1)
+    FP32GEMM_SPLIT_CASE(2)
+    FP32GEMM_SPLIT_CASE(3)
+    FP32GEMM_SPLIT_CASE(4)
+    FP32GEMM_SPLIT_CASE(5)
+    FP32GEMM_SPLIT_CASE(6)
+    FP32GEMM_SPLIT_CASE(7)
+    FP32GEMM_SPLIT_CASE(8)
+#undef FP32GEMM_SPLIT_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The pipeline: 8 waves, 4 rows per pass, 4 passes in flight (128 KB of W
+// per workgroup).  FORCE_SERIAL: the scratch-free form even when a slot is
+// free (tests).
+constexpr int kSplitNW = 8, kSplitU = 4, kSplitD = 4;
+constexpr int kSplitStep = kSplitNW * kSplitU * kSplitD;
+
+template <bool FORCE_SERIAL>
+hipError_t launch_split(const GemmArgs &a, int transA, hipStream_t s) {
+  if (!gemv_supported(a, transA) || a.batch != 1) return hipErrorInvalidValue;
+  const SplitPlan p = split_plan(a.N, a.K, kSplitMaxGroups, kSplitStep);
+  const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
+  int slot = -1;
+  if (!FORCE_SERIAL && p.ncb * p.S <= kSplitMaxGroups) slot = split_slot(s);
+  constexpr int NW = kSplitNW, U = kSplitU, D = kSplitD;
+  if (slot >= 0)
+    return vec ? launch_split_m<true, NW, U, D, false>(a, transA, p, slot, s)
+               : launch_split_m<false, NW, U, D, false>(a, transA, p, slot, s);
+  return vec ? launch_split_m<true, NW, U, D, true>(a, transA, p, -1, s)
+             : launch_split_m<false, NW, U, D, true>(a, transA, p, -1, s);
+}
+
+}  // namespace
+
+// Where the split kernel is chosen (W stored K x N, one product): timed
+// against the column-stripe and skinny kernels over 25 swept shapes, cold
+// weights.  For M <= 4 it wins from about 12 M weights on (M = 1: 3072 x
+// 4096 13.3 against 18.2 us; 4096^2 16.3 against 17.9; 4096 x 11008 34.7
+// against 43.9; 2048 x 8192 17.0 against 30.4) and loses on small products
+// (2048^2: 7.5 against 6.1), where its fixed cost (partial sums, counter,
+// final sum: about 2 us) is a larger share.  For M = 5..8 the skinny MFMA
+// kernel keeps most shapes (4096^2: 20.2 against 21.1; 8192^2: 48.0
+// against 50.6); the split wins where K is long against few column blocks
+// (4096 x 11008: 39.7 against 48.9).  Above 64 column blocks the other
+// kernels have enough workgroups without a split (1 x 32000 x 4096: 93.2
+// against 96.9).
+bool gemv_split_pays(int M, int N, int K, int batch) {
+  if (batch != 1 || M < 1 || M > kSplitMaxRowsM) return false;
+  const SplitPlan p = split_plan(N, K, kSplitMaxGroups, kSplitStep);
+  if (p.S < 2 || p.ncb * p.S > kSplitMaxGroups || p.ncb > 64) return false;
+  const long long w = (long long)N * K;
+  if (M <= 4) return w >= (12LL << 20);
+  return p.ncb <= 16 && w >= (32LL << 20);
+}
+
+hipError_t launch_gemv_split(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<false>(a, transA, s);
+}
+hipError_t launch_gemv_split_serial(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<true>(a, transA, s);
+}
+
+}  // namespace fp32gemm

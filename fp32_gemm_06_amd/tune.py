@@ -58,6 +58,18 @@ SHAPES = [
     ("gemv", 1, 16384, 4096, 1.0, 0.0),
     ("gemv", 1, 32000, 4096, 1.0, 0.0),
     ("gemv", 1, 65536, 1024, 1.0, 0.0),
+    ("gemv", 2, 4096, 4096, 1.0, 0.0),
+    ("gemv", 1, 3072, 4096, 1.0, 0.0),
+    ("gemv", 1, 6144, 4096, 1.0, 0.0),
+    ("gemv", 4, 11008, 4096, 1.0, 0.0),
+    ("gemv", 4, 4096, 11008, 1.0, 0.0),
+    ("gemv", 1, 4096, 8192, 1.0, 0.0),
+    ("gemv", 1, 2048, 8192, 1.0, 0.0),
+    ("gemv", 1, 14336, 4096, 1.0, 0.0),
+    ("gemv", 1, 4096, 14336, 1.0, 0.0),
+    ("gemv", 8, 8192, 8192, 1.0, 0.0),
+    ("gemv", 4, 16384, 4096, 1.0, 0.0),
+    ("gemv", 8, 14336, 4096, 1.0, 0.0),
 ]
 
 

@@ -37,9 +37,10 @@
  *    unknown configuration id; a positive hipError_t value when a HIP call or
  *    kernel launch fails.  Nothing is enqueued when a negative code is
  *    returned.
- *  - Threads: every entry point is reentrant and keeps no per-call state;
- *    calls on different streams may run concurrently.  The library allocates
- *    no device memory.
+ *  - Threads: every entry point is reentrant; calls on different streams
+ *    may run concurrently.  The library allocates no device memory at run
+ *    time; the split-K decode kernel (see sgemv) uses device memory reserved
+ *    statically when the library is loaded, per stream.
  */
 #ifndef FP32GEMM_H
 #define FP32GEMM_H
@@ -73,13 +74,28 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
 /*
  * The same operation for 1 <= M <= 128 (the decode shape: X = A is M x K, the
  * weight W = B is K x N, Y = C is M x N; M is the number of sequences
- * decoded at once).  Bandwidth-bound: each workgroup streams a narrow block
- * of W's columns over all of K, its waves split K, and the partial sums are
- * added inside the workgroup in a fixed order (deterministic, no workspace,
- * no atomics).  Up to M = 32 the multiply can run on the vector ALUs
- * (128-bit loads of W), up to M = 128 on the matrix cores (16-column
- * stripes, v_mfma_f32_16x16x4_f32); the library picks by shape.  Returns -1
- * when M is outside 1..128.
+ * decoded at once).  Bandwidth-bound: the time is one pass over W.  The
+ * library picks the kernel by shape:
+ *  - large W with few 256-column blocks (for example 4096 x 4096 at
+ *    M <= 4): K is split across workgroups, each reading 1 KB runs of W's
+ *    rows over a chunk of K; the chunks' partial sums are added in chunk
+ *    order by the last workgroup of each column block, in the same kernel.
+ *    The partial sums and arrival counters live in device memory the
+ *    library reserves statically (about 16 MB per device, in 8 slots); each
+ *    stream gets its own slot on its first call, so calls on different
+ *    streams never share one.  Calls on further streams run a form without
+ *    scratch that adds the same partial sums in the same order
+ *    (bit-identical results).  A call captured in a HIP graph keeps the
+ *    capturing stream's slot: two replays of it must not run concurrently
+ *    with each other or with calls on that stream.
+ *  - otherwise each workgroup streams a narrow block of W's columns over
+ *    all of K, its waves split K, and the partial sums are added inside the
+ *    workgroup; up to M = 32 the multiply can run on the vector ALUs
+ *    (128-bit loads of W), up to M = 128 on the matrix cores (16-column
+ *    stripes, v_mfma_f32_16x16x4_f32).
+ * Every path adds in a fixed order (integer atomics only, none on floats),
+ * so repeated calls give bit-identical results.  Returns -1 when M is
+ * outside 1..128.
  */
 int sgemv(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,

@@ -134,6 +134,8 @@ def test_gemv_batch_range(lib):
         # the others 8
         if name.startswith("mfma"):
             assert rows[cfg] == {"16": 128, "32": 128, "64": 64}[name[4:6]], name
+        elif name.startswith("split"):
+            assert rows[cfg] == 8, name
         else:
             waves, unroll = (int(v[1:]) for v in name.split("_")[1:3])
             assert rows[cfg] == (32 if unroll == 4 and waves <= 8 else 8), name
@@ -282,22 +284,37 @@ def test_model_choices():
     assert name(288, 11008, 4096) == "64x64x32_w32x32_m16_g8"
 
 
+def test_split_gemv_choice():
+    """K split across workgroups for large weights with few 256-column
+    blocks: from about 12 M weights at M <= 4, from 32 M with at most 16
+    column blocks at M = 5..8; not for small products or above 64 column
+    blocks."""
+    name = lambda *s: fg.fp32gemm_config_name(1, fg.fp32gemm_select_config(1, *s))
+    for shape in [(1, 4000, 4096), (1, 4608, 4096), (4, 4096, 4096), (1, 4096, 11008),
+                  (8, 4096, 11008), (6, 4000, 9000), (2, 16384, 4096), (1, 8192, 8192)]:
+        assert name(*shape) == "split256_w8_u4", shape
+    for shape in [(1, 2048, 2048), (1, 1024, 1024), (8, 4000, 4096), (1, 32000, 4096),
+                  (1, 16640, 4096), (8, 8192, 8192), (7, 14000, 4096)]:
+        assert not name(*shape).startswith("split"), shape
+
+
 def test_stripe_width_by_rounds():
     """Column-stripe and skinny widths: the narrowest stripe whose grid needs
     the fewest rounds of 256 workgroups (weighted by the wider stripes' cost
     per workgroup), within each configuration's row limit."""
     name = lambda *s: fg.fp32gemm_config_name(1, fg.fp32gemm_select_config(1, *s))
-    # M <= 8: 16 columns while one round holds the grid (N <= 4096), then 32, then 64
-    assert name(1, 4000, 4096) == "c16_w8_u4"
-    assert name(4, 4000, 4096) == "c16_w4_u8"
+    # M <= 8 below the split kernel's size: 16 columns while one round
+    # holds the grid (N <= 4096), then 32, then 64
+    assert name(1, 4000, 2048) == "c16_w8_u4"
+    assert name(4, 4000, 2048) == "c16_w4_u8"
     for N in (4608, 6144, 7168):
-        assert name(1, N, 4096) == "c32_w8_u4", N
-    assert name(1, 9216, 4096) == "c64_w8_u4"
-    assert name(8, 16384, 4096) == "c64_w8_u4"
+        assert name(1, N, 1024) == "c32_w8_u4", N
+    assert name(1, 9216, 1024) == "c64_w8_u4"
+    assert name(8, 16384, 1024) == "c64_w8_u4"
     # M = 5..8 on the skinny kernel while its stripes fit one round
-    assert name(8, 4000, 4096) == "mfma16_w8"
+    assert name(8, 4000, 2048) == "mfma16_w8"
     assert name(6, 8192, 2048) == "mfma32_w8"
-    assert name(8, 9216, 4096) == "c64_w8_u4"
+    assert name(8, 9216, 1024) == "c64_w8_u4"
     # skinny kernel: 64-column stripes up to M = 64, 32-column up to 128
     assert name(16, 4096, 4096) == "mfma16_w8"
     assert name(48, 4608, 4096) == "mfma32_w8"
