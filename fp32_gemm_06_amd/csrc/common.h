@@ -132,9 +132,13 @@ int gemv_stripe_blocks(int N, int batch);
 // dispatcher takes it for this shape (one product, M <= 8).  The
 // _serial form walks the chunks in one workgroup per column block and needs
 // no scratch; its results are bit-identical.
+// gemv_split_waves: the pipeline for the shape's chunk length (4 or 8 waves).
 bool gemv_split_pays(int M, int N, int K, int batch);
-hipError_t launch_gemv_split(const GemmArgs &a, int transA, hipStream_t s);
-hipError_t launch_gemv_split_serial(const GemmArgs &a, int transA, hipStream_t s);
+int gemv_split_waves(int N, int K);
+hipError_t launch_gemv_split4(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_gemv_split4_serial(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_gemv_split8(const GemmArgs &a, int transA, hipStream_t s);
+hipError_t launch_gemv_split8_serial(const GemmArgs &a, int transA, hipStream_t s);
 
 // Small-M product with op(B) = B^T (B stored N x K): row-dot kernel.
 // rows_per_wave is 1 or 2; <= 0 picks from M.

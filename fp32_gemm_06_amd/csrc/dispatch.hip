@@ -276,7 +276,8 @@ int select_gemv_config_batched(int M, int N, int K, int batch) {
   // W of 16 M floats and more with few column blocks: K split across
   // workgroups in 1 KB runs of each row (gemv_split.hip).
   if (gemv_split_pays(M, N, K, batch)) {
-    const int id = find_gemv("split256_w8_u4");
+    const int id =
+        find_gemv(gemv_split_waves(N, K) == 4 ? "split256_w4_u4" : "split256_w8_u4");
     if (id >= 0) return id;
   }
   // From M = 5 on, while its stripes fit one round of workgroups, the skinny

@@ -88,7 +88,8 @@ int split_slot(hipStream_t s) {
 // Workgroup (column block cb, chunk s): rows [s KC, (s + 1) KC) of K, 256
 // columns.  Wave w of a pass takes U consecutive rows, each wave instruction
 // one 1 KB run of a row (lane l: columns 4 l .. 4 l + 3).  D passes of
-// loads are in flight while one is multiplied.  Workgroup ids run over the
+// loads are in flight while one is multiplied; the chunk's passes run in
+// blocks of D, starting at a block that depends on the column block.  Workgroup ids run over the
 // chunks of one column block first; the hardware deals consecutive ids to
 // the 8 XCDs in turn, so each XCD streams whole rows of its chunks (timed
 // at 4096 x 4096, M = 1, against consecutive column blocks of one chunk:
@@ -167,9 +168,14 @@ gemv_split_kernel(GemmArgs a, int transA, int S, int KC, int slot) {
         xr[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
       }
     }
+    // the chunk's blocks of D passes start at a phase that depends on the
+    // column block, so the column blocks of one chunk do not all read the
+    // same rows at the same time
+    const int nblk = KC / (D * ROWS);
+    const int phase = (cb % 4) * nblk / 4;
     float w[D][U][4];
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_w(w[d], d * ROWS);
+    for (int d = 0; d < D; ++d) load_w(w[d], phase * D * ROWS + d * ROWS);
     __syncthreads();  // the previous chunk's sums have been read (SERIAL)
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
@@ -198,13 +204,16 @@ gemv_split_kernel(GemmArgs a, int transA, int S, int KC, int slot) {
         }
     };
     // KC is a multiple of D passes; each multiply frees its registers for
-    // the pass D ahead (past the chunk: out-of-range offsets, no traffic)
-    for (int r0 = 0; r0 < KC; r0 += D * ROWS) {
+    // the pass D ahead (after the last block: out-of-range offsets, no
+    // traffic)
+    for (int it = 0; it < nblk; ++it) {
+      const int r0 = ((it + phase) % nblk) * D * ROWS;
+      const int rn = it + 1 < nblk ? ((it + 1 + phase) % nblk) * D * ROWS : KC + D * ROWS;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         multiply(w[d], r0 + d * ROWS);
         __builtin_amdgcn_sched_barrier(0);
-        load_w(w[d], r0 + (d + D) * ROWS);
+        load_w(w[d], rn + d * ROWS);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -247,27 +256,31 @@ gemv_split_kernel(GemmArgs a, int transA, int S, int KC, int slot) {
     if (!last) return;
     asm volatile("" ::: "memory");
     const float *ws = &g_split_partials[slot][(size_t)cb * S * OUTS];
-    // chunks in order; the loads of a group are issued together, so a group
-    // costs one memory round trip
-    constexpr int G = 16;
+    // chunks in order; the loads of a group (about 32 per thread, over all
+    // of the thread's outputs) are issued together, so a group costs one
+    // memory round trip
+    constexpr int G = 32 / OPT > 0 ? 32 / OPT : 1;
+    bool mine[OPT];
 #pragma unroll
     for (int j = 0; j < OPT; ++j) {
       const int o = tid + j * THREADS;
-      if ((OUTS % THREADS == 0 || o < OUTS) && n0 + o % CW < N) {
-        float t = 0.0f;
-        for (int s0 = 0; s0 < S; s0 += G) {
-          float v[G];
+      mine[j] = (OUTS % THREADS == 0 || o < OUTS) && n0 + o % CW < N;
+    }
+    for (int s0 = 0; s0 < S; s0 += G) {
+      float v[OPT][G];
 #pragma unroll
-          for (int i = 0; i < G; ++i)
-            v[i] = s0 + i < S ? __hip_atomic_load(&ws[(size_t)(s0 + i) * OUTS + o],
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.0f;
+      for (int j = 0; j < OPT; ++j)
 #pragma unroll
-          for (int i = 0; i < G; ++i)
-            if (s0 + i < S) t = s0 + i == 0 ? v[i] : t + v[i];
-        }
-        total[j] = t;
-      }
+        for (int i = 0; i < G; ++i)
+          v[j][i] = (mine[j] & (s0 + i < S))
+                        ? __hip_atomic_load(&ws[(size_t)(s0 + i) * OUTS + tid + j * THREADS],
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : 0.0f;
+#pragma unroll
+      for (int j = 0; j < OPT; ++j)
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+          if (s0 + i < S) total[j] = s0 + i == 0 ? v[j][i] : total[j] + v[j][i];
     }
     if (tid == 0)
       __hip_atomic_store(&g_split_counters[slot][cb], 0u, __ATOMIC_RELAXED,
@@ -333,20 +346,27 @@ hipError_t launch_split_m(const GemmArgs &a, int transA, const SplitPlan &p, int
   return hipGetLastError();
 }
 
-// The pipeline: 8 waves, 4 rows per pass, 4 passes in flight (128 KB of W
-// per workgroup).  FORCE_SERIAL: the scratch-free form even when a slot is
+// Two pipelines, 4 rows per pass and 4 passes in flight: 4 waves (64 KB
+// of W in flight per workgroup) or 8 waves (128 KB).  Timed at 4096 x 4096,
+// M = 1, cold, in one run: 14.7 us on 4 waves against 15.2 on 8, and
+// 16.0 / 15.7 without the phases; phases on every pass instead of every 4
+// passes took 22 us.  Between GPUs the two pipelines trade places by a few
+// per cent (4096^2: 15.8 / 16.1 us on another); the swept shapes take the
+// faster one from the per-shape table, other shapes 4 waves for chunks of
+// up to 256 rows and 8 beyond (4096 x 8192, M = 1: 26.9 us on 8 against
+// 28.8 on 4).  FORCE_SERIAL: the scratch-free form even when a slot is
 // free (tests).
-constexpr int kSplitNW = 8, kSplitU = 4, kSplitD = 4;
-constexpr int kSplitStep = kSplitNW * kSplitU * kSplitD;
+constexpr int kSplitU = 4, kSplitD = 4;
+constexpr int kSplitStep = 8 * kSplitU * kSplitD;  // chunk granularity, both pipelines
 
-template <bool FORCE_SERIAL>
+template <int NW, bool FORCE_SERIAL>
 hipError_t launch_split(const GemmArgs &a, int transA, hipStream_t s) {
   if (!gemv_supported(a, transA) || a.batch != 1) return hipErrorInvalidValue;
   const SplitPlan p = split_plan(a.N, a.K, kSplitMaxGroups, kSplitStep);
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
   int slot = -1;
   if (!FORCE_SERIAL && p.ncb * p.S <= kSplitMaxGroups) slot = split_slot(s);
-  constexpr int NW = kSplitNW, U = kSplitU, D = kSplitD;
+  constexpr int U = kSplitU, D = kSplitD;
   if (slot >= 0)
     return vec ? launch_split_m<true, NW, U, D, false>(a, transA, p, slot, s)
                : launch_split_m<false, NW, U, D, false>(a, transA, p, slot, s);
@@ -377,11 +397,21 @@ bool gemv_split_pays(int M, int N, int K, int batch) {
   return p.ncb <= 16 && w >= (32LL << 20);
 }
 
-hipError_t launch_gemv_split(const GemmArgs &a, int transA, hipStream_t s) {
-  return launch_split<false>(a, transA, s);
+int gemv_split_waves(int N, int K) {
+  return split_plan(N, K, kSplitMaxGroups, kSplitStep).KC <= 256 ? 4 : 8;
 }
-hipError_t launch_gemv_split_serial(const GemmArgs &a, int transA, hipStream_t s) {
-  return launch_split<true>(a, transA, s);
+
+hipError_t launch_gemv_split4(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<4, false>(a, transA, s);
+}
+hipError_t launch_gemv_split4_serial(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<4, true>(a, transA, s);
+}
+hipError_t launch_gemv_split8(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<8, false>(a, transA, s);
+}
+hipError_t launch_gemv_split8_serial(const GemmArgs &a, int transA, hipStream_t s) {
+  return launch_split<8, true>(a, transA, s);
 }
 
 }  // namespace fp32gemm

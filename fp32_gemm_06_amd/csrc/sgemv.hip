@@ -540,8 +540,10 @@ const GemvConfig *gemv_configs(int *count) {
       {"mfma16_w8", 16, 8, 0, 128, &launch_skinny16},
       {"mfma32_w8", 32, 8, 0, 128, &launch_skinny32},
       {"mfma64_w8", 64, 8, 0, 64, &launch_skinny64},
-      {"split256_w8_u4", 256, 8, 4, 8, &launch_gemv_split},
-      {"split256_w8_u4_serial", 256, 8, 4, 8, &launch_gemv_split_serial},
+      {"split256_w4_u4", 256, 4, 4, 8, &launch_gemv_split4},
+      {"split256_w4_u4_serial", 256, 4, 4, 8, &launch_gemv_split4_serial},
+      {"split256_w8_u4", 256, 8, 4, 8, &launch_gemv_split8},
+      {"split256_w8_u4_serial", 256, 8, 4, 8, &launch_gemv_split8_serial},
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

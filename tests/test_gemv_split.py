@@ -25,38 +25,43 @@ def _cfg(name):
     return names.index(name)
 
 
+VARIANTS = ["split256_w4_u4", "split256_w8_u4"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("shape", SHAPES, ids=str)
-def test_split_matches_scratch_free_form_and_oracle(shape):
+def test_split_matches_scratch_free_form_and_oracle(shape, variant):
     require_gpu()
     M, N, K = shape
     A, B, C0 = inputs.random_case(M * 1000 + N + K, M, N, K, kind="normal")
-    split, canary = run_hip(A, B, C0, 0.75, -0.5, config=_cfg("split256_w8_u4"), family="gemv",
+    split, canary = run_hip(A, B, C0, 0.75, -0.5, config=_cfg(variant), family="gemv",
                             guard=32)
     assert canary, "write outside C"
-    serial, _ = run_hip(A, B, C0, 0.75, -0.5, config=_cfg("split256_w8_u4_serial"),
+    serial, _ = run_hip(A, B, C0, 0.75, -0.5, config=_cfg(variant + "_serial"),
                         family="gemv")
     assert np.array_equal(split, serial), f"{shape}: split and scratch-free forms differ"
     assert_parity(split, oracle.sgemm(A, B, C0, 0.75, -0.5), oracle.bound(A, B, C0, 0.75, -0.5),
                   f"split {shape}")
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("shape", [(1, 4096, 4096), (8, 1000, 777), (4, 333, 4099)], ids=str)
-def test_split_integer_exact(shape):
+def test_split_integer_exact(shape, variant):
     require_gpu()
     M, N, K = shape
     A, B, C0 = inputs.random_case(M + N + K, M, N, K, kind="int")
-    got, canary = run_hip(A, B, C0, 1.0, 0.5, config=_cfg("split256_w8_u4"), family="gemv",
-                          guard=32)
+    got, canary = run_hip(A, B, C0, 1.0, 0.5, config=_cfg(variant), family="gemv", guard=32)
     assert canary
     assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"int {shape}")
 
 
-def test_repeated_calls_reset_the_counters():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_repeated_calls_reset_the_counters(variant):
     """Calls back to back on one stream with new inputs each time, shapes
     with different chunk counts in between: each equals the scratch-free form."""
     torch = require_gpu()
     dev = torch.device("cuda:0")
-    split, serial = _cfg("split256_w8_u4"), _cfg("split256_w8_u4_serial")
+    split, serial = _cfg(variant), _cfg(variant + "_serial")
     for i, (M, N, K) in enumerate([(1, 4096, 4096), (8, 4096, 4096), (2, 1000, 777),
                                    (1, 4096, 4096), (5, 2048, 8192), (1, 4096, 4096)] * 2):
         g = inputs.rng(500 + i)
@@ -72,14 +77,15 @@ def test_repeated_calls_reset_the_counters():
         assert torch.equal(outs[0], outs[1]), f"call {i} {(M, N, K)}"
 
 
-def test_more_streams_than_scratch_slots():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_more_streams_than_scratch_slots(variant):
     """Twelve streams (the library keeps scratch for eight per device) run
     the product at once on different inputs; the streams without scratch
     take the scratch-free form.  Every result equals the scratch-free form
     computed alone."""
     torch = require_gpu()
     dev = torch.device("cuda:0")
-    split, serial = _cfg("split256_w8_u4"), _cfg("split256_w8_u4_serial")
+    split, serial = _cfg(variant), _cfg(variant + "_serial")
     M, N, K = 4, 4096, 4096
     streams = [torch.cuda.Stream() for _ in range(12)]
     Xs, Ws, Ys = [], [], []
