@@ -22,6 +22,7 @@ _lib = None
 KIND_SGEMM = 0
 KIND_SGEMV = 1
 ERR_CONFIG = -100
+ERR_SCRATCH = -101
 
 _GEMM_ARGTYPES = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
@@ -42,10 +43,12 @@ ACT_NONE = 0
 ACT_RELU = 1
 _SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
+_SPLITK_NOALLOC_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p]
 
 # Every symbol include/fp32gemm.h declares.
 EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_fused", "sgemm_splitk",
-           "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits", "fp32gemm_strerror",
+           "sgemm_splitk_noalloc", "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits",
+           "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
            "fp32gemm_config_max_rows", "fp32gemm_round_split", "fp32gemm_sgemm_with_config",
            "fp32gemm_sgemv_with_config")
@@ -76,6 +79,8 @@ def lib():
         L.sgemm_fused.restype = ctypes.c_int
         L.sgemm_splitk.argtypes = _SPLITK_ARGTYPES
         L.sgemm_splitk.restype = ctypes.c_int
+        L.sgemm_splitk_noalloc.argtypes = _SPLITK_NOALLOC_ARGTYPES
+        L.sgemm_splitk_noalloc.restype = ctypes.c_int
         L.sgemm_splitk_workspace_size.argtypes = [ctypes.c_int] * 4
         L.sgemm_splitk_workspace_size.restype = ctypes.c_size_t
         L.fp32gemm_splitk_splits.argtypes = [ctypes.c_int] * 3
@@ -160,6 +165,14 @@ def sgemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
     return lib().sgemm_splitk(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
                               _addr(C), ldc, splits, _addr(workspace), workspace_bytes,
                               _stream(stream))
+
+
+def sgemm_splitk_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                         stream=None) -> int:
+    """sgemm_splitk with the partial products in the library's static
+    device scratch (no allocation; at most 4 Mi floats of partials)."""
+    return lib().sgemm_splitk_noalloc(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B),
+                                      ldb, beta, _addr(C), ldc, splits, _stream(stream))
 
 
 def sgemm_splitk_workspace_size(M, N, K, splits=0) -> int:

@@ -3,6 +3,8 @@
 // The host-side launch mirrors the pages' launch step (grid over C tiles,
 // asynchronous launch that returns at once; "CUDA 矩阵乘法优化", section
 // "1. Kernel 1: 朴素实现"), with the grid shape taken from the chosen tile.
+#include <mutex>
+
 #include "../../include/fp32gemm.h"
 #include "common.h"
 
@@ -149,6 +151,59 @@ int run_product(int ta, int tb, const GemmArgs &a, hipStream_t s) {
   return run_tiled(ta, tb, a, s);
 }
 
+// Split-K as two kernels over a workspace of chunks x M x N floats (packed
+// planes): chunk c of K as batch entry c, raw sums into plane c, then
+// C <- alpha * (the planes added in order) + beta * C.
+int run_splitk(int transA, int transB, const GemmArgs &a, int chunks, int kc, float *workspace,
+               hipStream_t s) {
+  const int M = a.M, N = a.N;
+  GemmArgs p = a;
+  p.K = kc;
+  p.k_total = a.K;
+  p.alpha = 1.0f;
+  p.beta = 0.0f;
+  p.C = workspace;
+  p.ldc = N;
+  p.sA = transA ? (long long)kc * a.lda : (long long)kc;
+  p.sB = transB ? (long long)kc : (long long)kc * a.ldb;
+  p.sC = (long long)M * N;
+  p.batch = chunks;
+  const int rc = run_gemm(model_gemm_config(M, N, kc, chunks, nullptr), transA, transB, p, s);
+  if (rc) return rc;
+  return (int)launch_splitk_reduce(workspace, chunks, M, N, a.alpha, a.beta, a.C, a.ldc, s);
+}
+
+// ---- scratch of sgemm_splitk_noalloc ---------------------------------------
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the split-K partial products go
+// to this file-scope array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the array's name only stands for the device symbol; its device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is passed to kernels.
+constexpr size_t kScratchFloats = (size_t)4 << 20;  // 16 MiB
+__device__ __attribute__((aligned(256))) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
               int ldb, float beta, float *C, int ldc) {
   GemmArgs a;
@@ -258,22 +313,30 @@ int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha, const
   if (chunks <= 1) return run_product(transA, transB, a, s);  // the plain routine, no workspace
   if (workspace == nullptr) return -15;
   if (workspace_bytes < (size_t)chunks * (size_t)M * (size_t)N * sizeof(float)) return -16;
-  // phase 1: chunk c of K as batch entry c, raw sums into workspace plane c
-  GemmArgs p = a;
-  p.K = kc;
-  p.k_total = K;
-  p.alpha = 1.0f;
-  p.beta = 0.0f;
-  p.C = workspace;
-  p.ldc = N;
-  p.sA = transA ? (long long)kc * lda : (long long)kc;
-  p.sB = transB ? (long long)kc : (long long)kc * ldb;
-  p.sC = (long long)M * N;
-  p.batch = chunks;
-  rc = run_gemm(model_gemm_config(M, N, kc, chunks, nullptr), transA, transB, p, s);
+  return run_splitk(transA, transB, a, chunks, kc, workspace, s);
+}
+
+int sgemm_splitk_noalloc(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                         int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                         int splits, fp32gemm_stream_t stream) {
+  GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  int rc = check_args(kPosSgemmEx, transA, transB, a);
   if (rc) return rc;
-  // phase 2: C <- alpha * (sum of the planes, in order) + beta * C
-  return (int)launch_splitk_reduce(workspace, chunks, M, N, alpha, beta, C, ldc, s);
+  if (splits < 0 || splits > kMaxSplits) return -14;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int kc = 0;
+  const bool work = a.M > 0 && a.N > 0 && a.alpha != 0.0f && a.K > 0;
+  const int chunks =
+      !work || M <= 8 ? 1 : splitk_chunk(K, splits > 0 ? splits : splitk_pick(M, N, K), &kc);
+  // checked before anything is enqueued, quick returns included
+  if (chunks > 1 && (size_t)chunks * (size_t)M * (size_t)N > kScratchFloats)
+    return FP32GEMM_ERR_SCRATCH;
+  if (quick_return(a, s, &rc)) return rc;
+  if (chunks <= 1) return run_product(transA, transB, a, s);  // no scratch needed
+  float *ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return (int)e;
+  return run_splitk(transA, transB, a, chunks, kc, ws, s);
 }
 
 const char *fp32gemm_strerror(int code) {
@@ -286,6 +349,9 @@ const char *fp32gemm_strerror(int code) {
       "invalid argument 16", "invalid argument 17", "invalid argument 18"};
   if (code == 0) return "success";
   if (code == FP32GEMM_ERR_CONFIG) return "unknown configuration id";
+  if (code == FP32GEMM_ERR_SCRATCH)
+    return "the split-K partial products exceed the 16 MiB static scratch of "
+           "sgemm_splitk_noalloc (chunks x M x N floats must be at most 4 Mi)";
   if (code < 0 && code >= -18) return bad[-code - 1];
   if (code > 0) return hipGetErrorString(static_cast<hipError_t>(code));
   return "unknown error code";

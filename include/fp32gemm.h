@@ -55,6 +55,7 @@ typedef struct ihipStream_t *fp32gemm_stream_t;
 
 #define FP32GEMM_OK 0
 #define FP32GEMM_ERR_CONFIG (-100)
+#define FP32GEMM_ERR_SCRATCH (-101)
 
 /*
  * C[M x N] <- alpha * A[M x K] . B[K x N] + beta * C.
@@ -198,6 +199,34 @@ int sgemm_splitk(int transA, int transB, int M, int N, int K, float alpha,
                  const float *A, int lda, const float *B, int ldb, float beta,
                  float *C, int ldc, int splits, float *workspace,
                  size_t workspace_bytes, fp32gemm_stream_t stream);
+
+/*
+ * sgemm_splitk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and summation order as sgemm_splitk with the
+ * same splits (bit-identical results), but the partial products go to a
+ * scratch array the library holds in device memory, 16 MiB on each GPU it
+ * runs on, kept until the process ends.  No hipMalloc, hipFree or other
+ * allocating call is made.
+ *
+ * Limit: chunks x M x N floats (the chunk count as sgemm_splitk would use
+ * it, see sgemm_splitk_workspace_size / 4) must be at most 4 Mi; larger
+ * calls return FP32GEMM_ERR_SCRATCH and enqueue nothing.  Calls that need
+ * no scratch (one chunk, M <= 8, quick returns) run as sgemm_ex does.
+ *
+ * All calls on one GPU share its scratch array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (on different streams,
+ * or graph replays running concurrently) race and give undefined results.
+ * Calls in sequence on one stream are safe.
+ *
+ * Argument positions for error codes: transA 1, transB 2, M 3, N 4, K 5,
+ * alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12, ldc 13, splits 14,
+ * stream 15.
+ */
+int sgemm_splitk_noalloc(int transA, int transB, int M, int N, int K,
+                         float alpha, const float *A, int lda, const float *B,
+                         int ldb, float beta, float *C, int ldc, int splits,
+                         fp32gemm_stream_t stream);
 
 /* Workspace bytes sgemm_splitk needs for this shape and splits (0 = the
  * library's choice); 0 when the call runs as a single chunk. */

@@ -202,6 +202,28 @@ def test_splitk_argument_checks_need_no_gpu(lib):
     assert call_sk(alpha=0.0, beta=1.0, A=None, B=None) == 0
 
 
+def test_splitk_noalloc_checks_need_no_gpu(lib):
+    """The no-allocation split-K: argument errors and the scratch limit are
+    reported before anything is enqueued."""
+    def f(**kw):
+        a = dict(SK)
+        a.update(kw)
+        return fg.sgemm_splitk_noalloc(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"],
+                                       a["A"], a["lda"], a["B"], a["ldb"], a["beta"], a["C"],
+                                       a["ldc"], a["splits"], 0)
+    assert f(ta=3) == -1
+    assert f(K=-1) == -5
+    assert f(lda=100) == -8
+    assert f(splits=-1) == -14
+    assert f(splits=70000) == -14
+    assert f(C=None) == -12
+    # 4 chunks x 2048 x 2048 floats = 16 Mi > the 4 Mi scratch
+    assert f(M=2048, N=2048, lda=4096, ldb=2048, ldc=2048) == fg.ERR_SCRATCH
+    assert "16 MiB" in fg.strerror(fg.ERR_SCRATCH)
+    assert f(M=0, A=None, B=None, C=None) == 0
+    assert f(alpha=0.0, beta=1.0, A=None, B=None) == 0
+
+
 def test_splitk_workspace_size(lib):
     ws = fg.sgemm_splitk_workspace_size
     assert ws(64, 64, 4096, 4) == 4 * 64 * 64 * 4
