@@ -15,6 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
+# the HBM streaming probe (measurement only, its own library)
+PROBE_SOURCE = "hbm_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 SOURCES = ["api.hip", "dispatch.hip", "sgemm_configs.hip", "sgemm_nn.hip", "sgemm_nt.hip",
            "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip", "gemv_split.hip", "skinny.hip",
            "splitk.hip"]
@@ -48,15 +51,20 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(jobs: int = 8) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
+    _link(objs[-1:], PROBE_LIB)
+    return _link(objs[:-1], LIB)
 
 
 if __name__ == "__main__":
