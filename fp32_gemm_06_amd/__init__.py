@@ -44,11 +44,13 @@ ACT_RELU = 1
 _SPLITK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
 _SPLITK_NOALLOC_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_int, ctypes.c_void_p]
+_STREAMK_ARGTYPES = _EX_ARGTYPES[:-1] + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
 # Every symbol include/fp32gemm.h declares.
 EXPORTS = ("sgemm", "sgemv", "sgemm_ex", "sgemm_strided_batched", "sgemm_fused", "sgemm_splitk",
            "sgemm_splitk_noalloc", "sgemm_splitk_workspace_size", "fp32gemm_splitk_splits",
-           "fp32gemm_strerror",
+           "sgemm_streamk", "sgemm_streamk_workspace_size", "fp32gemm_streamk_tile_name",
+           "fp32gemm_streamk_plan", "fp32gemm_streamk_with_config", "fp32gemm_strerror",
            "fp32gemm_num_configs", "fp32gemm_config_name", "fp32gemm_select_config",
            "fp32gemm_config_max_rows", "fp32gemm_round_split", "fp32gemm_sgemm_with_config",
            "fp32gemm_sgemv_with_config")
@@ -81,6 +83,16 @@ def lib():
         L.sgemm_splitk.restype = ctypes.c_int
         L.sgemm_splitk_noalloc.argtypes = _SPLITK_NOALLOC_ARGTYPES
         L.sgemm_splitk_noalloc.restype = ctypes.c_int
+        L.sgemm_streamk.argtypes = _STREAMK_ARGTYPES
+        L.sgemm_streamk.restype = ctypes.c_int
+        L.sgemm_streamk_workspace_size.argtypes = [ctypes.c_int] * 3
+        L.sgemm_streamk_workspace_size.restype = ctypes.c_size_t
+        L.fp32gemm_streamk_tile_name.argtypes = [ctypes.c_int]
+        L.fp32gemm_streamk_tile_name.restype = ctypes.c_char_p
+        L.fp32gemm_streamk_plan.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)] * 3
+        L.fp32gemm_streamk_plan.restype = ctypes.c_size_t
+        L.fp32gemm_streamk_with_config.argtypes = [ctypes.c_int, ctypes.c_int] + _STREAMK_ARGTYPES
+        L.fp32gemm_streamk_with_config.restype = ctypes.c_int
         L.sgemm_splitk_workspace_size.argtypes = [ctypes.c_int] * 4
         L.sgemm_splitk_workspace_size.restype = ctypes.c_size_t
         L.fp32gemm_splitk_splits.argtypes = [ctypes.c_int] * 3
@@ -173,6 +185,39 @@ def sgemm_splitk_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C
     device scratch (no allocation; at most 4 Mi floats of partials)."""
     return lib().sgemm_splitk_noalloc(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B),
                                       ldb, beta, _addr(C), ldc, splits, _stream(stream))
+
+
+def sgemm_streamk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                  workspace_bytes, stream=None) -> int:
+    """sgemm_ex as one stream-K grid; the caller provides the workspace
+    (sgemm_streamk_workspace_size bytes)."""
+    return lib().sgemm_streamk(transA, transB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                               _addr(C), ldc, _addr(workspace), workspace_bytes, _stream(stream))
+
+
+def sgemm_streamk_workspace_size(M, N, K) -> int:
+    return lib().sgemm_streamk_workspace_size(M, N, K)
+
+
+def fp32gemm_streamk_tile_name(tile: int):
+    s = lib().fp32gemm_streamk_tile_name(tile)
+    return None if s is None else s.decode()
+
+
+def fp32gemm_streamk_plan(M, N, K, tile=-1, groups=0):
+    """(workspace bytes, tile, workgroups, K slices per workgroup) of the
+    stream-K plan for this shape (tile -1 / groups 0: the library's choice)."""
+    t, g, i = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0)
+    b = lib().fp32gemm_streamk_plan(M, N, K, tile, groups, ctypes.byref(t), ctypes.byref(g),
+                                    ctypes.byref(i))
+    return b, t.value, g.value, i.value
+
+
+def fp32gemm_streamk_with_config(tile, groups, transA, transB, M, N, K, alpha, A, lda, B, ldb,
+                                 beta, C, ldc, workspace, workspace_bytes, stream=None) -> int:
+    return lib().fp32gemm_streamk_with_config(tile, groups, transA, transB, M, N, K, alpha,
+                                              _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                                              _addr(workspace), workspace_bytes, _stream(stream))
 
 
 def sgemm_splitk_workspace_size(M, N, K, splits=0) -> int:

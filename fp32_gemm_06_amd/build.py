@@ -20,7 +20,7 @@ PROBE_SOURCE = "hbm_probe.hip"
 PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 SOURCES = ["api.hip", "dispatch.hip", "sgemm_configs.hip", "sgemm_nn.hip", "sgemm_nt.hip",
            "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip", "gemv_split.hip", "skinny.hip",
-           "splitk.hip"]
+           "splitk.hip", "streamk.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

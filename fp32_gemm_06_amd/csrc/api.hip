@@ -219,6 +219,26 @@ GemmArgs pack(int M, int N, int K, float alpha, const float *A, int lda, const f
   return a;
 }
 
+// Stream-K call shared by sgemm_streamk and its forced-plan hook; `base` is
+// the 1-based position of transA in the caller's parameter list.
+int streamk_call(int tile, int groups, int base, int transA, int transB, int M, int N, int K,
+                 float alpha, const float *A, int lda, const float *B, int ldb, float beta,
+                 float *C, int ldc, float *workspace, size_t workspace_bytes, hipStream_t s,
+                 bool forced) {
+  GemmArgs a = pack(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  const int off = base - 1;
+  const Pos p = {1 + off, 2 + off, 3 + off, 4 + off, 5 + off, 7 + off, 8 + off, 0,
+                 9 + off, 10 + off, 0, 12 + off, 13 + off, 0, 0};
+  int rc = check_args(p, transA, transB, a);
+  if (rc) return rc;
+  if (quick_return(a, s, &rc)) return rc;
+  if (!forced && M <= 8) return run_product(transA, transB, a, s);  // the GEMV kernels
+  const SkPlan plan = streamk_plan(M, N, K, tile, groups);
+  if (plan.tile < 0) return FP32GEMM_ERR_CONFIG;
+  if (workspace == nullptr) return -(14 + off);
+  if (workspace_bytes < streamk_workspace_bytes(plan)) return -(15 + off);
+  return (int)launch_streamk(transA, transB, a, plan, workspace, s);
+}
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -339,6 +359,42 @@ int sgemm_splitk_noalloc(int transA, int transB, int M, int N, int K, float alph
   return run_splitk(transA, transB, a, chunks, kc, ws, s);
 }
 
+size_t sgemm_streamk_workspace_size(int M, int N, int K) {
+  if (M <= 8 || N <= 0 || K <= 0) return 0;
+  return streamk_workspace_bytes(streamk_plan(M, N, K, -1, 0));
+}
+
+int sgemm_streamk(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                  int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                  float *workspace, size_t workspace_bytes, fp32gemm_stream_t stream) {
+  return streamk_call(-1, 0, 1, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), false);
+}
+
+size_t fp32gemm_streamk_plan(int M, int N, int K, int tile, int groups, int *tile_out,
+                             int *groups_out, int *ipw_out) {
+  if (M <= 0 || N <= 0 || K <= 0 || tile < -1 || tile >= streamk_num_tiles() || groups < 0)
+    return 0;
+  const SkPlan p = streamk_plan(M, N, K, tile, groups);
+  if (tile_out) *tile_out = p.tile;
+  if (groups_out) *groups_out = p.groups;
+  if (ipw_out) *ipw_out = p.ipw;
+  return streamk_workspace_bytes(p);
+}
+
+const char *fp32gemm_streamk_tile_name(int tile) { return streamk_tile_name(tile); }
+
+int fp32gemm_streamk_with_config(int tile, int groups, int transA, int transB, int M, int N,
+                                 int K, float alpha, const float *A, int lda, const float *B,
+                                 int ldb, float beta, float *C, int ldc, float *workspace,
+                                 size_t workspace_bytes, fp32gemm_stream_t stream) {
+  if (tile < -1 || tile >= streamk_num_tiles()) return FP32GEMM_ERR_CONFIG;
+  if (groups < 0) return -2;
+  return streamk_call(tile, groups, 3, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                      ldc, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                      true);
+}
+
 const char *fp32gemm_strerror(int code) {
   static const char *const bad[] = {
       "invalid argument 1",  "invalid argument 2",  "invalid argument 3",
@@ -347,7 +403,9 @@ const char *fp32gemm_strerror(int code) {
       "invalid argument 10", "invalid argument 11", "invalid argument 12",
       "invalid argument 13", "invalid argument 14", "invalid argument 15",
       "invalid argument 16", "invalid argument 17", "invalid argument 18"};
+  static const char *const bad_high[] = {"invalid argument 19", "invalid argument 20"};
   if (code == 0) return "success";
+  if (code == -19 || code == -20) return bad_high[-code - 19];
   if (code == FP32GEMM_ERR_CONFIG) return "unknown configuration id";
   if (code == FP32GEMM_ERR_SCRATCH)
     return "the split-K partial products exceed the 16 MiB static scratch of "

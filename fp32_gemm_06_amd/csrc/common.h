@@ -75,6 +75,20 @@ inline bool vec4_ok(const GemmArgs &a, bool ta, bool tb) {
   return okA && okB && a.k_total % 4 == 0;
 }
 
+// Scratch slots kept per (device, stream): a stream gets slot 0..7 on its
+// first call that needs one, and keeps it; -1 when all are taken.
+constexpr int kStreamSlots = 8;
+int stream_slot(hipStream_t s);
+
+// Stream-K work assignment of the tiled kernel (sgemm_kernel.h): workgroup g
+// takes units [g ipw, (g + 1) ipw) of the tile-major (tile, K slice) units;
+// part holds 2 x grid partial tiles, cnt one arrival counter per tile.
+struct SkArgs {
+  int ipw;
+  float *part;
+  unsigned *cnt;
+};
+
 // ---- SGEMM (fp32 MFMA) family ---------------------------------------------
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs &, bool dma, int group_m, hipStream_t);
 struct GemmConfig {
@@ -89,6 +103,13 @@ void launchers_nn(GemmLaunchFn *out);
 void launchers_nt(GemmLaunchFn *out);
 void launchers_tn(GemmLaunchFn *out);
 void launchers_tt(GemmLaunchFn *out);
+// Stream-K launchers of the tiles in FP32GEMM_SK_TILES, same order.
+typedef hipError_t (*SkLaunchFn)(const GemmArgs &, bool dma, int group_m, int groups,
+                                 const SkArgs &, hipStream_t);
+void sk_launchers_nn(SkLaunchFn *out);
+void sk_launchers_nt(SkLaunchFn *out);
+void sk_launchers_tn(SkLaunchFn *out);
+void sk_launchers_tt(SkLaunchFn *out);
 
 // ---- GEMV (M <= 32) family ------------------------------------------------
 struct GemvConfig {
@@ -155,6 +176,20 @@ int splitk_chunk(int K, int splits, int *kc);
 int splitk_pick(int M, int N, int K);
 hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, float alpha, float beta,
                                 float *C, int ldc, hipStream_t s);
+
+// Stream-K (streamk.hip): plan (tile index into FP32GEMM_SK_TILES, number of
+// workgroups, units per workgroup, tiles of C; tile -1 when none), the
+// workspace it needs, and the launch.  tile < 0 / groups <= 0 choose.
+struct SkPlan {
+  int tile, groups, ipw;
+  long long tiles;
+};
+SkPlan streamk_plan(int M, int N, int K, int tile, int groups);
+size_t streamk_workspace_bytes(const SkPlan &p);
+hipError_t launch_streamk(int ta, int tb, const GemmArgs &a, const SkPlan &p, float *workspace,
+                          hipStream_t s);
+int streamk_num_tiles();
+const char *streamk_tile_name(int t);
 
 // SGEMM configuration ids combine a tile shape with the tile-ordering group
 // (tile-rows per strip): id = tile_index * kNumGroups + group_index.

@@ -51,14 +51,13 @@ namespace {
 constexpr int kSplitCW = 256;          // columns per workgroup (64 lanes x float4)
 constexpr int kSplitMaxRowsM = 8;      // largest M
 constexpr int kSplitMaxGroups = 256;   // column blocks x chunks per call with scratch
-constexpr int kSplitSlots = 8;         // streams per device with their own scratch
 constexpr int kSplitKcMax = 1024;      // rows of K per chunk (X chunk staged in LDS)
 
 // Partial sums: [column block][chunk][row m][column], MR rows per call.
 __device__ __attribute__((aligned(256)))
-float g_split_partials[kSplitSlots][(size_t)kSplitMaxGroups * kSplitMaxRowsM * kSplitCW];
+float g_split_partials[kStreamSlots][(size_t)kSplitMaxGroups * kSplitMaxRowsM * kSplitCW];
 // Arrival counters, one per column block; zero between calls.
-__device__ __attribute__((aligned(256))) unsigned g_split_counters[kSplitSlots][kSplitMaxGroups] =
+__device__ __attribute__((aligned(256))) unsigned g_split_counters[kStreamSlots][kSplitMaxGroups] =
     {};
 
 // Stream -> slot, per device.  Slots are never released: a stream keeps its
@@ -70,7 +69,9 @@ struct SlotOwner {
 };
 std::vector<SlotOwner> g_slot_owners;
 
-int split_slot(hipStream_t s) {
+}  // namespace
+
+int stream_slot(hipStream_t s) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   std::lock_guard<std::mutex> lk(g_slot_mu);
@@ -80,10 +81,12 @@ int split_slot(hipStream_t s) {
     if (o.stream == s) return used;
     ++used;
   }
-  if (used >= kSplitSlots) return -1;
+  if (used >= kStreamSlots) return -1;
   g_slot_owners.push_back({dev, s});
   return used;
 }
+
+namespace {
 
 // Workgroup (column block cb, chunk s): rows [s KC, (s + 1) KC) of K, 256
 // columns.  Wave w of a pass takes U consecutive rows, each wave instruction
@@ -365,7 +368,7 @@ hipError_t launch_split(const GemmArgs &a, int transA, hipStream_t s) {
   const SplitPlan p = split_plan(a.N, a.K, kSplitMaxGroups, kSplitStep);
   const bool vec = ((uintptr_t)a.B % 16 == 0) && a.N % 4 == 0 && a.ldb % 4 == 0;
   int slot = -1;
-  if (!FORCE_SERIAL && p.ncb * p.S <= kSplitMaxGroups) slot = split_slot(s);
+  if (!FORCE_SERIAL && p.ncb * p.S <= kSplitMaxGroups) slot = stream_slot(s);
   constexpr int U = kSplitU, D = kSplitD;
   if (slot >= 0)
     return vec ? launch_split_m<true, NW, U, D, false>(a, transA, p, slot, s)

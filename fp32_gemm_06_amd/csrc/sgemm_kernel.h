@@ -129,12 +129,22 @@ struct Operand {
   }
 };
 
-// The kernel: one BM x BN tile of C (of batch entry blockIdx.y) per workgroup.
-// DMA = 128-bit loads straight into LDS; otherwise 32-bit loads staged in
-// registers and written to the same LDS positions (any alignment).
-template <class T, bool TRANS_A, bool TRANS_B, bool DMA>
-__global__ void __launch_bounds__(T::NT)
-sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
+// Stream-K work assignment (SK kernels only, SkArgs in common.h).  The
+// product's tiles x nk K slices are numbered tile-major ("units"); logical
+// workgroup g (ids renumbered XCD by XCD, as for tiles) takes units
+// [g ipw, (g + 1) ipw).  A tile whose units several workgroups
+// share is finished by the last of them to arrive, which adds the others'
+// raw partial tiles in K order.  part: 2 x grid partial tiles of BM x BN
+// floats (slot 2 g for a workgroup's first segment, 2 g + 1 for its last);
+// cnt: one arrival counter per tile, zero between calls.
+
+// The kernel: one BM x BN tile of C (of batch entry blockIdx.y) per workgroup,
+// or (SK) the stream-K units of workgroup blockIdx.x.  DMA = 128-bit loads
+// straight into LDS; otherwise 32-bit loads staged in registers and written
+// to the same LDS positions (any alignment).
+template <class T, bool TRANS_A, bool TRANS_B, bool DMA, bool SK = false>
+__global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(SK && T::WAVES <= 4 ? 4 : 1)))
+sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m, SkArgs sk) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, WAVES = T::WAVES;
   constexpr bool KCA = !TRANS_A;  // A as given is k-contiguous
   constexpr bool KCB = TRANS_B;   // B^T storage is k-contiguous
@@ -143,27 +153,24 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   constexpr int STAGE = OA::FLOATS + OB::FLOATS;
   constexpr int NS = DMA ? 2 * T::P : 2;  // LDS buffers
   __shared__ __attribute__((aligned(16))) float lds[NS * STAGE];
+  __shared__ int sk_last;  // stream-K: this workgroup finishes the tile
+  (void)sk_last;
 
   // ---- batch and C tile (XCD-aware order) ---------------------------------
-  // Workgroups are handed to the 8 XCDs round-robin by id; renumber them so
-  // that each XCD receives a contiguous range of logical ids, then walk the
-  // tiles in strips of group_m tile-rows so that the tiles an XCD runs
-  // together share A and B panels in its L2.
   const long long bz = blockIdx.y;
   const float *Ag = a.A + bz * a.sA;
   const float *Bg = a.B + bz * a.sB;
   float *Cg = a.C + bz * a.sC;
-  const int G = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, per = G >> 3, extra = G & 7;
-  const int lid = xcd * per + min(xcd, extra) + (bid >> 3);
-  const int width = group_m * tiles_n;
-  const int grp = lid / width;
-  const int first_m = grp * group_m;
-  const int gsz = min(tiles_m - first_m, group_m);
-  const int within = lid - grp * width;
-  const int m0 = (first_m + within % gsz) * BM;
-  const int n0 = (within / gsz) * BN;
+  // logical tile id -> tile origin, strips of group_m tile-rows
+  auto tile_origin = [&](int lid, int &m0, int &n0) {
+    const int width = group_m * tiles_n;
+    const int grp = lid / width;
+    const int first_m = grp * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    const int within = lid - grp * width;
+    m0 = (first_m + within % gsz) * BM;
+    n0 = (within / gsz) * BN;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,12 +180,63 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
   const int l32 = lane & 31, half = lane >> 5;
   const int c16 = lane & 15, q4 = lane >> 4;
 
-  const int rows = a.M - m0;  // valid rows of this tile (may exceed BM)
-  const int cols = a.N - n0;
   // split-K chunks: the last one may be shorter
   const int Kb = a.k_total > 0 ? min(a.K, a.k_total - (int)bz * a.K) : a.K;
-  const int nk = (Kb + BK - 1) / BK;
-  const int ktail = Kb - (nk - 1) * BK;  // valid k in the last slice, 1..BK
+  const int nk_tile = (Kb + BK - 1) / BK;
+  const int ktail_tile = Kb - (nk_tile - 1) * BK;  // valid k in the tile's last slice, 1..BK
+
+  // Workgroups are handed to the 8 XCDs round-robin by id; logical ids
+  // number them so that each XCD receives a contiguous range, so the tiles
+  // (or stream-K units) an XCD runs together are neighbours that share A
+  // and B panels in its L2.
+  const int G = gridDim.x;
+  const int xcd = (int)blockIdx.x & 7, per = G >> 3, extra = G & 7;
+  const int lid = xcd * per + min(xcd, extra) + ((int)blockIdx.x >> 3);
+
+  // Stream-K arrival bookkeeping.  A workgroup's first segment, when more
+  // segments follow, is published without waiting: its arrival at tile
+  // pend_t is counted after the next segment's first barrier (by then the
+  // partial-tile stores have completed), and if it turns out to be the last
+  // arrival, that tile is finished after this workgroup's other segments.
+  int pend_t = -1;           // tile of the first segment, arrival pending or counted
+  bool pend_sent = false;    // its arrival has been counted
+  bool pend_fix = false;     // ... and it was the last one
+  bool pend_done = false;    // pend_fix is known
+  unsigned pend_before = 0;  // (thread 0) the counter before that arrival
+  (void)pend_sent;
+  (void)pend_fix;
+  (void)pend_done;
+  (void)pend_before;
+  // segments (workgroups) that share tile t
+  auto nseg_of = [&](int t) -> int {
+    const long long u0 = (long long)t * nk_tile;
+    return (int)((u0 + nk_tile - 1) / sk.ipw - u0 / sk.ipw) + 1;
+  };
+  (void)nseg_of;
+  auto signal_pending = [&]() {
+    if (pend_t >= 0 && !pend_sent) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial tile is written
+      __syncthreads();
+      if (tid == 0)
+        pend_before = __hip_atomic_fetch_add(&sk.cnt[pend_t], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      pend_sent = true;
+    }
+  };
+  (void)signal_pending;
+
+  // One tile (origin m0, n0; tile id t for stream-K) over its K slices
+  // [kb, ke).  Stream-K: slot is the partial-tile slot of this segment,
+  // last_seg whether it ends the workgroup's units; kb == ke only finishes
+  // tile t from the published partial tiles.
+  auto run = [&](int m0, int n0, int kb, int ke, int t, int slot, bool last_seg) {
+  (void)t;
+  (void)slot;
+  (void)last_seg;
+  const int rows = a.M - m0;  // valid rows of this tile (may exceed BM)
+  const int cols = a.N - n0;
+  const int nk = ke - kb;                             // slices of this segment
+  const int ktail = ke == nk_tile ? ktail_tile : BK;  // valid k in its last slice
 
   // Source offset (bytes from the slice's base) of the first of this lane's
   // 4 floats per instruction, or kOob when the lane's storage row lies
@@ -213,12 +271,12 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
 
   // Slice bases: the tile origin moved to K slice ks.
   auto base_a = [&](int ks) -> const float * {
-    return KCA ? Ag + (size_t)m0 * a.lda + (size_t)ks * BK
-               : Ag + (size_t)ks * BK * a.lda + m0;
+    return KCA ? Ag + (size_t)m0 * a.lda + (size_t)(kb + ks) * BK
+               : Ag + (size_t)(kb + ks) * BK * a.lda + m0;
   };
   auto base_b = [&](int ks) -> const float * {
-    return KCB ? Bg + (size_t)n0 * a.ldb + (size_t)ks * BK
-               : Bg + (size_t)ks * BK * a.ldb + n0;
+    return KCB ? Bg + (size_t)n0 * a.ldb + (size_t)(kb + ks) * BK
+               : Bg + (size_t)(kb + ks) * BK * a.ldb + n0;
   };
 
   // Staged path: registers between the global loads and the LDS writes.
@@ -410,6 +468,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
+  if (!SK || ke > kb) {
   if constexpr (DMA && T::P > 1) {
     // P slices per barrier.  Stage st is slices [st P, st P + P) in buffers
     // (st % 2) P .. (st % 2) P + P - 1.  The next stage's P fetches start at
@@ -430,6 +489,7 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     for (int u = 0; u < P; ++u) fetch_slice(u);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+    if constexpr (SK) signal_pending();
     read_frag(lds, g0, f0);
     for (int st = 0; st < nst; ++st) {
       float *base = lds + (st & 1) * P * STAGE;
@@ -465,12 +525,14 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
     commit(lds);
     if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+    if constexpr (SK) signal_pending();
     read_frag(lds, g0, f0);
     for (int kt = 0; kt < nk; ++kt) {
       const int c = kt & 1;
       slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
     }
   }
+  }  // main loop
 
   // ---- K groups: groups 1.. park their sums in LDS, group 0 adds them -----
   // The last slice ended with a barrier after every LDS read of the loop, so
@@ -498,6 +560,92 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
           for (int v = 0; v < T::ACCN; ++v) acc[i][j][v] += red[((i * T::TN + j) * T::ACCN + v) * 64];
+    }
+  }
+
+  // ---- stream-K: a tile that several workgroups share ------------------------
+  // Publish the raw partial tile with agent-scope atomic stores (written
+  // through the XCD's L2), wait for them, count the arrival; the last
+  // workgroup to arrive adds every segment's partial tile in K order (its
+  // own included, reloaded like the others) and goes on to the epilogue.  A
+  // first segment that more segments follow is counted later (pend_t).  No
+  // release/acquire fences (they would write back and invalidate the whole
+  // L2): every value that crosses workgroups is an agent-scope atomic.
+  if constexpr (SK) {
+    static_assert(T::KS == 1, "stream-K tiles have one K group");
+    constexpr int PER = T::TM * T::TN * T::ACCN * 64;  // floats per wave
+    constexpr int TILE = BM * BN;
+    if (kb != 0 || ke != nk_tile) {
+      if (ke > kb) {
+        float *mine = sk.part + (size_t)slot * TILE + wave * PER + lane;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < T::ACCN; ++v)
+              __hip_atomic_store(mine + ((i * T::TN + j) * T::ACCN + v) * 64, acc[i][j][v],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!last_seg) {
+          pend_t = t;
+          return;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+          const unsigned before = __hip_atomic_fetch_add(&sk.cnt[t], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+          int f = before == (unsigned)(nseg_of(t) - 1) ? 1 : 0;
+          if (pend_t >= 0 && pend_before == (unsigned)(nseg_of(pend_t) - 1)) f |= 2;
+          sk_last = f;
+        }
+        __syncthreads();
+        const int f = sk_last;
+        pend_done = true;
+        pend_fix = (f & 2) != 0;
+        if (!(f & 1)) return;
+        asm volatile("" ::: "memory");
+      }
+      // Finish tile t: segment js belongs to logical workgroup gfirst + js
+      // (its first segment when that workgroup's units start inside the
+      // tile, else its last).  R segments' loads are in flight at a time,
+      // added into acc strictly in K order.
+      const int ipw = sk.ipw;
+      const long long u0 = (long long)t * nk_tile;
+      const int gfirst = (int)(u0 / ipw);
+      const int nseg = nseg_of(t);
+      constexpr int R = 2;
+      for (int j0 = 0; j0 < nseg; j0 += R) {
+        acc_t part[R][T::TM][T::TN];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (j0 + r < nseg) {
+            const int g = gfirst + j0 + r;
+            const int sl = 2 * g + ((long long)g * ipw >= u0 ? 0 : 1);
+            const float *src = sk.part + (size_t)sl * TILE + wave * PER + lane;
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+              for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < T::ACCN; ++v)
+                  part[r][i][j][v] = __hip_atomic_load(src + ((i * T::TN + j) * T::ACCN + v) * 64,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (j0 + r < nseg) {
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+              for (int j = 0; j < T::TN; ++j)
+                acc[i][j] = j0 + r == 0 ? part[r][i][j] : acc[i][j] + part[r][i][j];
+          }
+        }
+      }
+      if (tid == 0)
+        __hip_atomic_store(&sk.cnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -556,6 +704,43 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m) {
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v), 0, 0);
         }
   }
+  };  // run
+
+  if constexpr (!SK) {
+    // the logical id is the tile, walked in strips of group_m tile-rows
+    int m0, n0;
+    tile_origin(lid, m0, n0);
+    run(m0, n0, 0, nk_tile, 0, 0, true);
+  } else {
+    // logical workgroup lid's units, split at tile boundaries into
+    // segments; only the first and the last segment can be partial tiles
+    const long long total = (long long)tiles_m * tiles_n * nk_tile;
+    const long long ub = (long long)lid * sk.ipw;
+    const long long ue = min(ub + sk.ipw, total);
+    for (long long u = ub; u < ue;) {
+      const int t = (int)(u / nk_tile);
+      const int kb = (int)(u - (long long)t * nk_tile);
+      const int ke = (int)min((long long)nk_tile, kb + (ue - u));
+      int m0, n0;
+      tile_origin(t, m0, n0);
+      run(m0, n0, kb, ke, t, 2 * lid + (u == ub ? 0 : 1), u + (ke - kb) >= ue);
+      u += ke - kb;
+    }
+    if (pend_t >= 0) {
+      if (!pend_done) {
+        // the last segment was a whole tile: its first barrier counted the
+        // pending arrival; thread 0 holds the counter's old value
+        if (tid == 0) sk_last = pend_before == (unsigned)(nseg_of(pend_t) - 1) ? 2 : 0;
+        __syncthreads();
+        pend_fix = (sk_last & 2) != 0;
+      }
+      if (pend_fix) {
+        int m0, n0;
+        tile_origin(pend_t, m0, n0);
+        run(m0, n0, 0, 0, pend_t, 0, true);
+      }
+    }
+  }
 }
 
 // Launch one tile shape for one operand-layout combination.
@@ -567,10 +752,31 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
   if (G > 0x7fffffffLL || a.batch > 65535) return hipErrorInvalidConfiguration;
   if (group_m < 1) group_m = 1;
   const dim3 grid((unsigned)G, (unsigned)a.batch);
+  const SkArgs none = {0, nullptr, nullptr};
   if (dma)
-    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, true>), grid, dim3(T::NT), 0, s, a, tm, tn, group_m);
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, true>), grid, dim3(T::NT), 0, s, a, tm, tn,
+                       group_m, none);
   else
-    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, false>), grid, dim3(T::NT), 0, s, a, tm, tn, group_m);
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, false>), grid, dim3(T::NT), 0, s, a, tm,
+                       tn, group_m, none);
+  return hipGetLastError();
+}
+
+// Stream-K launch of one tile shape: `groups` workgroups of ipw units each
+// (the caller's plan: groups x ipw >= tiles x slices), one product.
+template <class T, bool TRANS_A, bool TRANS_B>
+hipError_t launch_sk(const GemmArgs &a, bool dma, int group_m, int groups, const SkArgs &sk,
+                     hipStream_t s) {
+  const int tm = (a.M + T::BM - 1) / T::BM;
+  const int tn = (a.N + T::BN - 1) / T::BN;
+  if (a.batch != 1 || a.k_total != 0 || groups < 1) return hipErrorInvalidValue;
+  if (group_m < 1) group_m = 1;
+  if (dma)
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, true, true>), dim3(groups), dim3(T::NT),
+                       0, s, a, tm, tn, group_m, sk);
+  else
+    hipLaunchKernelGGL((sgemm_kernel<T, TRANS_A, TRANS_B, false, true>), dim3(groups), dim3(T::NT),
+                       0, s, a, tm, tn, group_m, sk);
   return hipGetLastError();
 }
 
@@ -599,3 +805,12 @@ hipError_t launch(const GemmArgs &a, bool dma, int group_m, hipStream_t s) {
   X(64, 64, 32, 32, 32, 2, 2, 2, 32)     \
   X(32, 128, 32, 32, 32, 1, 1, 3, 32)    \
   X(64, 64, 32, 32, 32, 1, 1, 4, 16)
+// The tiles with a stream-K form (one K group, one slice per barrier); the
+// occupancy column is the stream-K kernel's own (its fix-up needs more
+// registers than the plain kernel: the 128x128 form fits one workgroup per
+// CU, the 64x64 form four, held there by its waves-per-SIMD attribute).
+// The 256x256 tile is not among them: with the fix-up's partial tiles live
+// its 8-wave form needs more than its 256 registers per lane and spills.
+#define FP32GEMM_SK_TILES(X)             \
+  X(128, 128, 32, 64, 32, 1, 1, 1, 32)   \
+  X(64, 64, 32, 32, 32, 1, 1, 4, 32)

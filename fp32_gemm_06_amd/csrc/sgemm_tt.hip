@@ -10,4 +10,11 @@ void launchers_tt(GemmLaunchFn *out) {
   for (size_t i = 0; i < sizeof(t) / sizeof(t[0]); ++i) out[i] = t[i];
 }
 #undef FP32GEMM_LAUNCHER
+#define FP32GEMM_SK_LAUNCHER(BM, BN, BK, WM, WN, KS, P, OCC, MF) \
+  &launch_sk<Tile<BM, BN, BK, WM, WN, KS, P, MF>, true, true>,
+void sk_launchers_tt(SkLaunchFn *out) {
+  const SkLaunchFn t[] = {FP32GEMM_SK_TILES(FP32GEMM_SK_LAUNCHER)};
+  for (size_t i = 0; i < sizeof(t) / sizeof(t[0]); ++i) out[i] = t[i];
+}
+#undef FP32GEMM_SK_LAUNCHER
 }  // namespace fp32gemm

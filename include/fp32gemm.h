@@ -228,6 +228,40 @@ int sgemm_splitk_noalloc(int transA, int transB, int M, int N, int K,
                          int ldb, float beta, float *C, int ldc, int splits,
                          fp32gemm_stream_t stream);
 
+/*
+ * Stream-K: the same product as sgemm_ex, as one persistent grid whose
+ * workgroups each take an equal run of the product's (C tile, K slice)
+ * units, crossing tile boundaries; a tile shared by several workgroups is
+ * finished in the same kernel by the last of them to arrive, which adds the
+ * others' partial tiles in K order and applies alpha, beta.  This is the
+ * pages' remedy for grids that leave compute units idle ("CUDA 矩阵乘法优化：
+ * 从朴素 Kernel 到接近 cuBLAS", section "10. cuBLAS 领先的性能差异": split
+ * K where the tiles of C alone do not fill the GPU), without split-K's
+ * second kernel and with every workgroup doing the same amount of work.
+ * Results are bit-reproducible (the order of the additions depends only on
+ * the shape).
+ *
+ * workspace: device memory owned by the caller, at least
+ * sgemm_streamk_workspace_size(M, N, K) bytes; it holds partial tiles (two
+ * per workgroup at most) and must not overlap A, B or C or be used by
+ * another call until this one has completed on its stream.  Arrival
+ * counters live in device memory the library reserves statically per
+ * stream (8 streams per device; beyond that they go to the end of the
+ * workspace, cleared by a small kernel before the main one).  M <= 8 runs
+ * the GEMV kernels as sgemm_ex does and needs no workspace.
+ *
+ * Argument positions for error codes: transA 1, transB 2, M 3, N 4, K 5,
+ * alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12, ldc 13, workspace 14
+ * (NULL), workspace_bytes 15 (too small), stream 16.
+ */
+int sgemm_streamk(int transA, int transB, int M, int N, int K, float alpha,
+                  const float *A, int lda, const float *B, int ldb, float beta,
+                  float *C, int ldc, float *workspace, size_t workspace_bytes,
+                  fp32gemm_stream_t stream);
+
+/* Workspace bytes sgemm_streamk needs for this shape (0 when M <= 8). */
+size_t sgemm_streamk_workspace_size(int M, int N, int K);
+
 /* Workspace bytes sgemm_splitk needs for this shape and splits (0 = the
  * library's choice); 0 when the call runs as a single chunk. */
 size_t sgemm_splitk_workspace_size(int M, int N, int K, int splits);
@@ -283,6 +317,27 @@ int fp32gemm_sgemv_with_config(int cfg, int M, int N, int K, float alpha,
                                const float *A, int lda, const float *B,
                                int ldb, float beta, float *C, int ldc,
                                fp32gemm_stream_t stream);
+
+/*
+ * Stream-K tuning and testing hooks.  Tiles are numbered 0 ..
+ * (number of names) - 1 and named by fp32gemm_streamk_tile_name (NULL past
+ * the end).  fp32gemm_streamk_plan reports the plan for a shape with a
+ * forced tile and / or workgroup count (-1 / 0 = the library's choice): the
+ * tile, workgroups and K slices per workgroup, and returns the workspace
+ * bytes it needs (0 for invalid arguments).  fp32gemm_streamk_with_config
+ * runs sgemm_streamk with that plan, for any M >= 1; error positions as
+ * sgemm_streamk shifted by two (tile 1, groups 2; FP32GEMM_ERR_CONFIG for an
+ * unknown tile).
+ */
+const char *fp32gemm_streamk_tile_name(int tile);
+size_t fp32gemm_streamk_plan(int M, int N, int K, int tile, int groups,
+                             int *tile_out, int *groups_out, int *ipw_out);
+int fp32gemm_streamk_with_config(int tile, int groups, int transA, int transB,
+                                 int M, int N, int K, float alpha,
+                                 const float *A, int lda, const float *B,
+                                 int ldb, float beta, float *C, int ldc,
+                                 float *workspace, size_t workspace_bytes,
+                                 fp32gemm_stream_t stream);
 
 #ifdef __cplusplus
 }

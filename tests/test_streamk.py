@@ -1,0 +1,168 @@
+"""Stream-K (sgemm_streamk): one persistent grid over the (tile, K slice)
+units, tiles shared by several workgroups finished by the last to arrive.
+
+Integer data makes every partial sum exact, so any split of a tile's K range
+over workgroups must reproduce the oracle bit for bit; forced plans with few
+workgroups make single workgroups span several tiles and cut tiles into many
+segments, with ragged M, N and K."""
+import numpy as np
+import pytest
+
+import fp32_gemm_06_amd as fg
+import oracle
+from fp32_gemm_06_amd import inputs
+from gpu_util import assert_bitexact, assert_parity, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 4321.0
+
+
+def _dev(torch, x, trans):
+    return torch.from_numpy(np.ascontiguousarray(x.T) if trans else x).to("cuda")
+
+
+def run_sk(A, B, C0, alpha, beta, ta=0, tb=0, tile=None, groups=0, stream=None, guard=16):
+    """Run stream-K on host arrays; returns (C as float64, canaries intact).
+    tile None = the library's plan through sgemm_streamk."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    dA, dB = _dev(torch, A, ta), _dev(torch, B, tb)
+    lda, ldb = (M if ta else K), (K if tb else N)
+    flat = torch.full((M * N + 2 * guard,), SENTINEL, device="cuda")
+    flat[guard:guard + M * N] = torch.from_numpy(C0.reshape(-1)).cuda()
+    C = flat[guard:guard + M * N]
+    if tile is None:
+        wsb = fg.sgemm_streamk_workspace_size(M, N, K)
+    else:
+        wsb = fg.fp32gemm_streamk_plan(M, N, K, tile, groups)[0]
+    ws = torch.empty(max(wsb, 4) // 4, device="cuda")
+    args = (ta, tb, M, N, K, alpha, dA, lda, dB, ldb, beta, C, N, ws, wsb)
+    if tile is None:
+        rc = fg.sgemm_streamk(*args, stream)
+    else:
+        rc = fg.fp32gemm_streamk_with_config(tile, groups, *args, stream)
+    if rc != 0:
+        raise fg.Fp32GemmError(rc)
+    torch.cuda.synchronize()
+    host = flat.cpu().numpy()
+    ok = bool(np.all(host[:guard] == SENTINEL)) and bool(np.all(host[guard + M * N:] == SENTINEL))
+    return host[guard:guard + M * N].reshape(M, N).astype(np.float64), ok
+
+
+def _ntiles():
+    n = 0
+    while fg.fp32gemm_streamk_tile_name(n) is not None:
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("groups", [1, 3, 7, 40, 0])
+def test_integer_exact_every_tile_and_split(tile, groups):
+    require_gpu()
+    M, N, K = 300, 520, 1000
+    A, B, C0 = inputs.random_case(tile * 100 + groups, M, N, K, kind="int")
+    got, ok = run_sk(A, B, C0, 1.0, 0.5, tile=tile, groups=groups)
+    assert ok, "write outside C"
+    _, t, g, ipw = fg.fp32gemm_streamk_plan(M, N, K, tile, groups)
+    assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5),
+                    f"tile {fg.fp32gemm_streamk_tile_name(tile)} groups {g} ipw {ipw}")
+
+
+@pytest.mark.parametrize("layout", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=str)
+def test_integer_exact_layouts_and_ragged_k(layout):
+    require_gpu()
+    ta, tb = layout
+    for (M, N, K, groups) in [(129, 67, 4099, 5), (64, 64, 33, 2), (200, 330, 2048, 0)]:
+        A, B, C0 = inputs.random_case(M + N + K, M, N, K, kind="int")
+        for tile in range(_ntiles()):
+            got, ok = run_sk(A, B, C0, 1.0, 0.5, ta=ta, tb=tb, tile=tile, groups=groups)
+            assert ok
+            assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5),
+                            f"{layout} {(M, N, K)} tile {tile} groups {groups}")
+
+
+def test_unaligned_operands_take_the_staged_path():
+    """K and N not multiples of 4: 32-bit loads, same result."""
+    require_gpu()
+    M, N, K = 70, 131, 517
+    A, B, C0 = inputs.random_case(5, M, N, K, kind="int")
+    for tile in range(_ntiles()):
+        got, ok = run_sk(A, B, C0, 1.0, 0.5, tile=tile, groups=9)
+        assert ok
+        assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"staged tile {tile}")
+
+
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1536, 1536, 1536), (256, 256, 8192),
+                                   (384, 4096, 1024)], ids=str)
+def test_library_plan_against_the_oracle(shape):
+    require_gpu()
+    M, N, K = shape
+    A, B, C0 = inputs.random_case(sum(shape), M, N, K, kind="uniform")
+    got, ok = run_sk(A, B, C0, 0.75, -1.25)
+    assert ok
+    assert_parity(got, oracle.sgemm(A, B, C0, 0.75, -1.25), oracle.bound(A, B, C0, 0.75, -1.25),
+                  f"stream-K {shape}")
+
+
+def test_deterministic_and_counters_reset():
+    """Back-to-back calls give identical bits; shapes with different tile
+    counts in between leave the counters at zero."""
+    require_gpu()
+    A, B, C0 = inputs.random_case(77, 520, 600, 3000, kind="normal")
+    first, _ = run_sk(A, B, C0, 1.0, 0.0, tile=0, groups=50)
+    for (tile, groups) in [(1, 7), (1, 100), (0, 50), (0, 50)]:
+        again, _ = run_sk(A, B, C0, 1.0, 0.0, tile=tile, groups=groups)
+        if (tile, groups) == (0, 50):
+            assert np.array_equal(first, again)
+
+
+def test_streams_beyond_the_counter_slots():
+    """Twelve streams at once (8 have reserved counters; the others use the
+    workspace's, cleared first): every result equals the single-stream one."""
+    torch = require_gpu()
+    M, N, K = 300, 400, 2000
+    A, B, C0 = inputs.random_case(31, M, N, K, kind="normal")
+    want, _ = run_sk(A, B, C0, 1.0, 0.5, tile=1, groups=37)
+    dA, dB = _dev(torch, A, 0), _dev(torch, B, 0)
+    wsb = fg.fp32gemm_streamk_plan(M, N, K, 1, 37)[0]
+    streams = [torch.cuda.Stream() for _ in range(12)]
+    Cs = [torch.from_numpy(C0).cuda() for _ in streams]
+    wss = [torch.empty(wsb // 4, device="cuda") for _ in streams]
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, st in enumerate(streams):
+            Cs[i].copy_(torch.from_numpy(C0).cuda())
+        torch.cuda.synchronize()
+        for i, st in enumerate(streams):
+            rc = fg.fp32gemm_streamk_with_config(1, 37, 0, 0, M, N, K, 1.0, dA, K, dB, N, 0.5,
+                                                 Cs[i], N, wss[i], wsb, st)
+            assert rc == 0, fg.strerror(rc)
+        torch.cuda.synchronize()
+        for i in range(len(streams)):
+            assert np.array_equal(Cs[i].cpu().numpy().astype(np.float64), want), (rep, i)
+
+
+def test_small_m_runs_the_gemv_path_without_workspace():
+    torch = require_gpu()
+    M, N, K = 4, 1000, 777
+    A, B, C0 = inputs.random_case(3, M, N, K, kind="int")
+    assert fg.sgemm_streamk_workspace_size(M, N, K) == 0
+    C = torch.from_numpy(C0).cuda()
+    rc = fg.sgemm_streamk(0, 0, M, N, K, 1.0, _dev(torch, A, 0), K, _dev(torch, B, 0), N, 0.5, C,
+                          N, None, 0)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert_bitexact(C.cpu().numpy().astype(np.float64), oracle.sgemm(A, B, C0, 1.0, 0.5), "M=4")
+
+
+def test_beta_zero_does_not_read_c():
+    require_gpu()
+    M, N, K = 100, 300, 700
+    A, B, _ = inputs.random_case(4, M, N, K, kind="int")
+    nanC = np.full((M, N), np.nan, dtype=np.float32)
+    got, ok = run_sk(A, B, nanC, 1.0, 0.0, tile=1, groups=11)
+    assert ok
+    assert_bitexact(got, oracle.sgemm(A, B, None, 1.0, 0.0), "beta = 0 over NaN")
