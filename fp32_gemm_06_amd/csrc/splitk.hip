@@ -6,10 +6,11 @@
 // 的性能差异").  On MI355X it pays for shapes whose C has few tiles but whose
 // K is long: the partial products multiply the number of workgroups, and the
 // extra traffic (each partial is written once and read once) is small next to
-// the K loop.  The cross-workgroup reduction is a second kernel rather than
-// an in-kernel "last workgroup adds" step: an agent-scope release/acquire
-// pair per workgroup writes back and invalidates the XCD's L2 on this GPU,
-// and a fixed summation order keeps results bit-reproducible.
+// the K loop.  The cross-workgroup reduction is a second kernel, so that
+// phase 1 is the batched tiled kernel unchanged for every tile shape and
+// layout, and its fixed summation order keeps results bit-reproducible.  The
+// in-kernel form, where the last workgroup of a tile adds the others' partial
+// tiles, is stream-K (streamk.hip).
 //
 // Phase 1 is the tiled kernel launched as a batch: entry s reads A and B
 // offset to chunk s and writes its raw sum to workspace plane s (packed

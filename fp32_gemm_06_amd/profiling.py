@@ -12,6 +12,12 @@ counter runs (pmc*/), each made with ``--output-format csv``.  Writes
 writes one table of this library's launches in a kernel-trace run, by kernel
 and launch shape (calls, mean and min duration).
 
+    python -m fp32_gemm_06_amd.profiling --pmc-table <run dir> <out.md> "<command>"
+
+writes the same table for counter runs (pmc*/ under <run dir>): the mean of
+each counter per dispatch by kernel and launch shape, and the L2 hit rate
+when TCC_HIT_sum and TCC_MISS_sum were collected.
+
     python -m fp32_gemm_06_amd.profiling --workload <run dir> <tag> <kernel needle>
         <skip> <count> <per step> <source files> <out dir> "<command>"
 
@@ -316,6 +322,47 @@ def trace_table(run_dir, out_md, command):
     return out_md
 
 
+def pmc_table(run_dir, out_md, command):
+    """Mean counter values per dispatch of this library's kernels, by kernel
+    and workgroup count, from `rocprofv3 --pmc ... --output-format csv`
+    runs under run_dir (every *counter_collection.csv below it)."""
+    hits = sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals, names = {}, set()
+    for path in hits:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if "fp32gemm::" not in r["Kernel_Name"]:
+                    continue
+                groups = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                key = (_short_kernel(r["Kernel_Name"]), groups, int(r["Workgroup_Size"]))
+                d = vals.setdefault(key, {})
+                d.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+                names.add(r["Counter_Name"])
+    names = sorted(names)
+    hit = "TCC_HIT_sum" in names and "TCC_MISS_sum" in names
+    lines = [f"# Counters: {os.path.basename(out_md)[:-3]}", "",
+             "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
+             "Mean per dispatch over every dispatch of the kernel with that workgroup count "
+             "(threads per workgroup in brackets)." +
+             (" L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS)." if hit else ""), "",
+             "| kernel | workgroups | dispatches | " + " | ".join(names) +
+             (" | L2 hit |" if hit else " |"),
+             "|---" * (3 + len(names) + hit) + "|"]
+    for (k, groups, wg), d in sorted(vals.items()):
+        n = max(len(v) for v in d.values())
+        means = {c: _avg(list(d[c].values())) if c in d else float("nan") for c in names}
+        row = f"| `{k}` | {groups} ({wg}) | {n} | " + " | ".join(f"{means[c]:.0f}" for c in names)
+        if hit:
+            h, m = means["TCC_HIT_sum"], means["TCC_MISS_sum"]
+            row += f" | {h / (h + m):.3f}"
+        lines.append(row + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_md
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "--workload":
         # --workload <run dir> <tag> <kernel needle> <skip> <count> <per step>
@@ -326,6 +373,8 @@ if __name__ == "__main__":
             print(w)
     elif sys.argv[1] == "--trace-table":
         print(trace_table(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif sys.argv[1] == "--pmc-table":
+        print(pmc_table(sys.argv[2], sys.argv[3], sys.argv[4]))
     else:
         for w in summarize(sys.argv[1], sys.argv[2], sys.argv[3]):
             print(w)

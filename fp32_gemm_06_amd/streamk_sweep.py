@@ -29,6 +29,9 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--md", default=None, help="also write a markdown table here")
     ap.add_argument("--shapes", nargs="*", default=None, help="MxNxK ...")
+    ap.add_argument("--configs", nargs="*", default=None,
+                    help="stream-K candidates as tile:groups (default: every tile at 256, "
+                         "512, 768 and 1024 workgroups)")
     a = ap.parse_args()
 
     import torch
@@ -66,6 +69,10 @@ def main():
     ntiles = 0
     while fg.fp32gemm_streamk_tile_name(ntiles) is not None:
         ntiles += 1
+    if a.configs:
+        cands = [tuple(int(v) for v in c.split(":")) for c in a.configs]
+    else:
+        cands = [(t, g) for t in range(ntiles) for g in (256, 512, 768, 1024)]
     big = torch.randn(4096, 4096, device=dev)   # warm the clock
     for _ in range(60):
         torch.matmul(big, big)
@@ -95,15 +102,14 @@ def main():
             rec["streamk_max_rel_err"] = float(((C.double() - ref).abs() /
                                                 (A.abs().double() @ B.abs().double())).max())
             del W
-            for tile in range(ntiles):
-                for groups in (256, 512, 768, 1024):
-                    wsb, _, g, ipw = fg.fp32gemm_streamk_plan(M, N, K, tile, groups)
-                    W = torch.empty(max(wsb // 4, 1), device=dev)
-                    rec[f"sk{tile}_g{groups}_us"] = timed(lambda: check(
-                        fg.fp32gemm_streamk_with_config(tile, groups, 0, 0, M, N, K, 1.0, A, K, B,
-                                                        N, 0.0, C, N, W, wsb, sp)))
-                    rec[f"sk{tile}_g{groups}_plan"] = f"g{g} ipw{ipw}"
-                    del W
+            for tile, groups in cands:
+                wsb, _, g, ipw = fg.fp32gemm_streamk_plan(M, N, K, tile, groups)
+                W = torch.empty(max(wsb // 4, 1), device=dev)
+                rec[f"sk{tile}_g{groups}_us"] = timed(lambda: check(
+                    fg.fp32gemm_streamk_with_config(tile, groups, 0, 0, M, N, K, 1.0, A, K, B, N,
+                                                    0.0, C, N, W, wsb, sp)))
+                rec[f"sk{tile}_g{groups}_plan"] = f"g{g} ipw{ipw}"
+                del W
             rec["vendor_us"] = timed(lambda: torch.matmul(A, B, out=C))
             for k in list(rec):
                 if k.endswith("_us"):
