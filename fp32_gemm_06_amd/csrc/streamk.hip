@@ -100,7 +100,6 @@ SkPlan streamk_plan(int M, int N, int K, int tile, int groups) {
   for (int t = 0; t < kNumSkTiles; ++t) {
     if (tile >= 0 && t != tile) continue;
     const long long tiles = tiles_of(t, M, N);
-    if (tile < 0 && tiles > kSkMaxTiles) continue;
     const long long units = tiles * nk;
     for (int w = 1; w <= kSkTiles[t].occ; ++w) {
       if (groups > 0 && w > 1) break;

@@ -242,6 +242,72 @@ def test_splitk_workspace_size(lib):
     assert ws(256, 256, 32768, 0) == s * 256 * 256 * 4
 
 
+def call_stk(**kw):
+    a = dict(SK, **kw)
+    return fg.sgemm_streamk(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                            a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["ws"],
+                            a["wsb"], 0)
+
+
+def test_streamk_argument_checks_need_no_gpu(lib):
+    """sgemm_streamk and its forced-plan hook report argument errors before
+    anything is enqueued (the hook's positions are shifted by its two leading
+    arguments)."""
+    need = fg.sgemm_streamk_workspace_size(64, 64, 4096)
+    assert need > 0
+    assert call_stk(ta=3) == -1
+    assert call_stk(K=-1) == -5
+    assert call_stk(lda=100) == -8
+    assert call_stk(C=None) == -12
+    assert call_stk() == -14                      # no workspace
+    assert call_stk(ws=16, wsb=need - 1) == -15  # too small
+    assert call_stk(M=0, A=None, B=None, C=None) == 0
+    assert call_stk(alpha=0.0, beta=1.0, A=None, B=None) == 0
+
+    def hook(tile, groups, **kw):
+        a = dict(SK, **kw)
+        return fg.fp32gemm_streamk_with_config(tile, groups, a["ta"], a["tb"], a["M"], a["N"],
+                                               a["K"], a["alpha"], a["A"], a["lda"], a["B"],
+                                               a["ldb"], a["beta"], a["C"], a["ldc"], a["ws"],
+                                               a["wsb"], 0)
+    assert hook(99, 0) == fg.ERR_CONFIG
+    assert hook(-2, 0) == fg.ERR_CONFIG
+    assert hook(0, -1) == -2
+    assert hook(0, 0, tb=5) == -4
+    assert hook(0, 0) == -16
+    assert hook(0, 0, ws=16, wsb=fg.fp32gemm_streamk_plan(64, 64, 4096, 0, 0)[0] - 1) == -17
+
+
+def _sk_tile_edge(t):
+    return int(fg.fp32gemm_streamk_tile_name(t).split("x")[0])
+
+
+@pytest.mark.parametrize("shape", [(768, 768, 768), (1024, 1024, 1024), (1536, 1536, 1536),
+                                   (384, 4096, 4096), (256, 256, 32768), (4160, 4160, 96),
+                                   (16384, 16384, 1024), (9, 5000, 33), (4092, 4092, 4092)])
+def test_streamk_plan_covers_every_unit(lib, shape):
+    """Every plan deals each (tile, K slice) unit to exactly one workgroup:
+    groups x ipw >= units > (groups - 1) x ipw, never more workgroups than
+    asked for, and the workspace holds two partial tiles per workgroup plus
+    one counter per tile."""
+    M, N, K = shape
+    for tile in (-1, 0, 1):
+        for groups in (0, 1, 7, 300, 10 ** 9):
+            wsb, t, g, ipw = fg.fp32gemm_streamk_plan(M, N, K, tile, groups)
+            assert t >= 0 and (tile < 0 or t == tile), (shape, tile, groups)
+            e = _sk_tile_edge(t)
+            tiles = -(-M // e) * -(-N // e)
+            units = tiles * -(-K // 32)
+            assert g >= 1 and g * ipw >= units > (g - 1) * ipw, (shape, tile, groups, g, ipw)
+            if groups:
+                assert g <= groups
+            assert wsb == (2 * g * e * e + tiles + 64) * 4
+    assert fg.sgemm_streamk_workspace_size(M, N, K) == (
+        fg.fp32gemm_streamk_plan(M, N, K)[0] if M > 8 else 0)
+    assert fg.sgemm_streamk_workspace_size(8, N, K) == 0
+    assert fg.fp32gemm_streamk_plan(0, N, K) == (0, -1, 0, 0)
+
+
 def test_fused_argument_checks_need_no_gpu(lib):
     def f(**kw):
         a = dict(EX, bias=None, act=0)

@@ -145,6 +145,22 @@ def test_streams_beyond_the_counter_slots():
             assert np.array_equal(Cs[i].cpu().numpy().astype(np.float64), want), (rep, i)
 
 
+def test_more_tiles_than_reserved_counters():
+    """4225 tiles of 64 x 64: past the 4096 reserved counters per stream, so the
+    arrival counters live in the workspace (cleared by the library first)."""
+    require_gpu()
+    M = N = 4160
+    K = 96
+    A, B, C0 = inputs.random_case(41, M, N, K, kind="int")
+    _, t, g, ipw = fg.fp32gemm_streamk_plan(M, N, K, 1, 0)
+    nk = -(-K // 32)
+    assert -(-M // 64) * -(-N // 64) > 4096 and ipw % nk != 0  # tiles are shared
+    for rep in range(2):
+        got, ok = run_sk(A, B, C0, 1.0, 0.5, tile=1, groups=0)
+        assert ok
+        assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"4225 tiles, call {rep}")
+
+
 def test_small_m_runs_the_gemv_path_without_workspace():
     torch = require_gpu()
     M, N, K = 4, 1000, 777
