@@ -2,7 +2,8 @@
 sgemm_streamk (the library's plan), every stream-K candidate (each tile at
 256, 512, 768 and 1024 workgroups: one to four per CU) and the vendor
 library, on shapes whose tiles fill the GPU badly (one to two rounds of
-tiles, or few tiles with a long K) and on larger ones.
+tiles, few tiles with a long K, decode batches of 48 to 288 rows) and on
+larger ones.  Operands stay resident between calls (no rotation of B).
 
 The worklog attributes part of the vendor BLAS's lead on such grids to
 splitting K ("CUDA 矩阵乘法优化：从朴素 Kernel 到接近 cuBLAS", section
@@ -21,6 +22,8 @@ import json
 SHAPES = [(768, 768, 768), (1024, 1024, 1024), (1024, 1024, 4096), (1536, 1536, 1536),
           (2000, 2000, 2000), (384, 4096, 4096), (512, 4096, 4096), (768, 4096, 4096),
           (256, 256, 32768), (512, 512, 8192), (1024, 1024, 16384), (160, 4096, 4096),
+          (48, 4096, 4096), (96, 11008, 4096), (128, 11008, 4096), (192, 11008, 4096),
+          (256, 11008, 4096), (288, 4096, 4096), (96, 4096, 11008),
           (2048, 11008, 4096), (3072, 3072, 3072), (4096, 4096, 4096)]
 
 
