@@ -10,7 +10,9 @@ splitting K ("CUDA 矩阵乘法优化：从朴素 Kernel 到接近 cuBLAS", sect
 "10. cuBLAS 领先的性能差异与全尺寸 Benchmark").  Same device buffers, alpha =
 1, beta = 0, fp32 with TF32 disabled; the vendor library is torch.matmul.
 The table also gives how much slower the library's plan is than the best
-candidate.
+candidate.  Its error column compares the plan's output with a float64 torch
+product on the GPU, a sanity check of the timed runs; parity against the
+oracle is tests/test_streamk.py.
 
     python -m fp32_gemm_06_amd.streamk_sweep --out sweep.jsonl --md table.md
 """
