@@ -32,8 +32,15 @@ def test_captured_sequence_replays_bit_identically():
     kc = torch.empty(H, S, D, device=dev)
     wsb = fg.sgemm_splitk_workspace_size(M, N, K, 4)
     ws = torch.empty(wsb // 4, device=dev)
+    # stream-K: the library's plan, and a forced one whose workgroups span
+    # several tiles and cut tiles into many segments
+    skb = fg.sgemm_streamk_workspace_size(M, N, K)
+    skw = torch.empty(skb // 4, device=dev)
+    skb2 = fg.fp32gemm_streamk_plan(M, N, K, 1, 37)[0]
+    skw2 = torch.empty(skb2 // 4, device=dev)
     outs = {name: torch.empty(shape, device=dev) for name, shape in (
-        ("sgemm", (M, N)), ("fused", (M, N)), ("splitk", (M, N)), ("gemv", (m, n)),
+        ("sgemm", (M, N)), ("fused", (M, N)), ("splitk", (M, N)), ("streamk", (M, N)),
+        ("streamk_forced", (M, N)), ("gemv", (m, n)),
         ("rows", (m, n)), ("scores", (H, 1, S)))}
 
     def fill(seed):
@@ -49,6 +56,9 @@ def test_captured_sequence_replays_bit_identically():
             fg.sgemm(M, N, K, 1.0, A, K, B, N, 0.5, o["sgemm"], N),
             fg.sgemm_fused(0, 0, M, N, K, 1.0, A, K, B, N, 0.5, o["fused"], N, bias, fg.ACT_RELU),
             fg.sgemm_splitk(0, 0, M, N, K, 1.0, A, K, B, N, 0.5, o["splitk"], N, 4, ws, wsb),
+            fg.sgemm_streamk(0, 0, M, N, K, 1.0, A, K, B, N, 0.5, o["streamk"], N, skw, skb),
+            fg.fp32gemm_streamk_with_config(1, 37, 0, 0, M, N, K, 1.0, A, K, B, N, 0.5,
+                                            o["streamk_forced"], N, skw2, skb2),
             fg.sgemv(m, n, k, 1.0, x, k, W, n, 0.5, o["gemv"], n),
             fg.sgemm_ex(0, 1, m, n, k, 1.0, x, k, Wt, k, 0.5, o["rows"], n),
             fg.sgemm_strided_batched(0, 1, 1, S, D, 0.088, q, D, D, kc, D, S * D, 0.5,
