@@ -88,6 +88,9 @@ int stream_slot(hipStream_t s) {
 
 namespace {
 
+// A compile-time count, to pass group sizes to a generic lambda.
+template <int V> struct Count { static constexpr int value = V; };
+
 // Workgroup (column block cb, chunk s): rows [s KC, (s + 1) KC) of K, 256
 // columns.  Wave w of a pass takes U consecutive rows, each wave instruction
 // one 1 KB run of a row (lane l: columns 4 l .. 4 l + 3).  D passes of
@@ -259,31 +262,42 @@ gemv_split_kernel(GemmArgs a, int transA, int S, int KC, int slot) {
     if (!last) return;
     asm volatile("" ::: "memory");
     const float *ws = &g_split_partials[slot][(size_t)cb * S * OUTS];
-    // chunks in order; the loads of a group (about 32 per thread, over all
-    // of the thread's outputs) are issued together, so a group costs one
-    // memory round trip
-    constexpr int G = 32 / OPT > 0 ? 32 / OPT : 1;
-    bool mine[OPT];
+    // Chunks in order, in groups of 16, 8, 4, 2 and 1 chunks (at most 64
+    // loads per thread, over all of the thread's outputs).  A group's loads
+    // have no conditions, so they are issued back to back and cost one
+    // memory round trip; the output index is clamped into this column
+    // block's partial sums (threads past OUTS load a valid value they do not
+    // use).
+    constexpr int GMAX = 64 / OPT >= 16 ? 16 : (64 / OPT > 0 ? 64 / OPT : 1);
+    auto group = [&](auto size, int s0) {
+      constexpr int GG = decltype(size)::value;
+      float v[OPT][GG];
 #pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int o = tid + j * THREADS;
-      mine[j] = (OUTS % THREADS == 0 || o < OUTS) && n0 + o % CW < N;
+      for (int j = 0; j < OPT; ++j) {
+        const int o = min(tid + j * THREADS, OUTS - 1);
+#pragma unroll
+        for (int i = 0; i < GG; ++i)
+          v[j][i] = __hip_atomic_load(&ws[(size_t)(s0 + i) * OUTS + o], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int j = 0; j < OPT; ++j)
+#pragma unroll
+        for (int i = 0; i < GG; ++i) total[j] = s0 + i == 0 ? v[j][i] : total[j] + v[j][i];
+    };
+    int s0 = 0;
+    for (; s0 + GMAX <= S; s0 += GMAX) group(Count<GMAX>{}, s0);
+    if constexpr (GMAX > 8) {
+      if (s0 + 8 <= S) group(Count<8>{}, s0), s0 += 8;
     }
-    for (int s0 = 0; s0 < S; s0 += G) {
-      float v[OPT][G];
-#pragma unroll
-      for (int j = 0; j < OPT; ++j)
-#pragma unroll
-        for (int i = 0; i < G; ++i)
-          v[j][i] = (mine[j] & (s0 + i < S))
-                        ? __hip_atomic_load(&ws[(size_t)(s0 + i) * OUTS + tid + j * THREADS],
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : 0.0f;
-#pragma unroll
-      for (int j = 0; j < OPT; ++j)
-#pragma unroll
-        for (int i = 0; i < G; ++i)
-          if (s0 + i < S) total[j] = s0 + i == 0 ? v[j][i] : total[j] + v[j][i];
+    if constexpr (GMAX > 4) {
+      if (s0 + 4 <= S) group(Count<4>{}, s0), s0 += 4;
+    }
+    if constexpr (GMAX > 2) {
+      if (s0 + 2 <= S) group(Count<2>{}, s0), s0 += 2;
+    }
+    if constexpr (GMAX > 1) {
+      if (s0 < S) group(Count<1>{}, s0);
     }
     if (tid == 0)
       __hip_atomic_store(&g_split_counters[slot][cb], 0u, __ATOMIC_RELAXED,
@@ -382,22 +396,23 @@ hipError_t launch_split(const GemmArgs &a, int transA, hipStream_t s) {
 // Where the split kernel is chosen (W stored K x N, one product): timed
 // against the column-stripe and skinny kernels over 25 swept shapes, cold
 // weights.  For M <= 4 it wins from about 12 M weights on (M = 1: 3072 x
-// 4096 13.3 against 18.2 us; 4096^2 16.3 against 17.9; 4096 x 11008 34.7
-// against 43.9; 2048 x 8192 17.0 against 30.4) and loses on small products
-// (2048^2: 7.5 against 6.1), where its fixed cost (partial sums, counter,
-// final sum: about 2 us) is a larger share.  For M = 5..8 the skinny MFMA
-// kernel keeps most shapes (4096^2: 20.2 against 21.1; 8192^2: 48.0
-// against 50.6); the split wins where K is long against few column blocks
-// (4096 x 11008: 39.7 against 48.9).  Above 64 column blocks the other
-// kernels have enough workgroups without a split (1 x 32000 x 4096: 93.2
-// against 96.9).
+// 4096 13.1 against 18.1 us; 4096^2 15.3 against 17.8; 4096 x 11008 33.1
+// against 43.7; 2048 x 8192 15.8 against 30.4) and loses on small products
+// (2048^2: 7.1 against 6.0), where its fixed cost (partial sums, counter,
+// final sum: about 2 us) is a larger share.  For M = 5..8 it wins while the
+// weight has at most 16 column blocks (4096^2, M = 8: 19.2 against 20.2 on
+// the skinny MFMA kernel; 4096 x 11008: 38.7 against 48.9); with more
+// column blocks the skinny kernel keeps it (8192^2: 48.0 against 50.1;
+// 11008 x 4096: 37.0 against 37.8).  Above 64 column blocks the other
+// kernels have enough workgroups without a split (1 x 32000 x 4096: 92.7
+// against 96.1).
 bool gemv_split_pays(int M, int N, int K, int batch) {
   if (batch != 1 || M < 1 || M > kSplitMaxRowsM) return false;
   const SplitPlan p = split_plan(N, K, kSplitMaxGroups, kSplitStep);
   if (p.S < 2 || p.ncb * p.S > kSplitMaxGroups || p.ncb > 64) return false;
   const long long w = (long long)N * K;
   if (M <= 4) return w >= (12LL << 20);
-  return p.ncb <= 16 && w >= (32LL << 20);
+  return p.ncb <= 16 && w >= (16LL << 20);
 }
 
 int gemv_split_waves(int N, int K) {

@@ -374,12 +374,13 @@ def test_model_choices():
 
 def test_split_gemv_choice():
     """K split across workgroups for large weights with few 256-column
-    blocks: from about 12 M weights at M <= 4, from 32 M with at most 16
+    blocks: from about 12 M weights at M <= 4, from 16 M with at most 16
     column blocks at M = 5..8; not for small products or above 64 column
     blocks."""
     name = lambda *s: fg.fp32gemm_config_name(1, fg.fp32gemm_select_config(1, *s))
     for shape in [(1, 4000, 4096), (1, 4608, 4096), (4, 4096, 4096), (1, 4096, 11008),
-                  (8, 4096, 11008), (6, 4000, 9000), (2, 16384, 4096), (1, 8192, 8192)]:
+                  (8, 4096, 11008), (6, 4000, 9000), (2, 16384, 4096), (1, 8192, 8192),
+                  (6, 4096, 4096), (8, 4096, 4096)]:
         assert name(*shape) in ("split256_w4_u4", "split256_w8_u4"), shape
     for shape in [(1, 2048, 2048), (1, 1024, 1024), (8, 4000, 4096), (1, 32000, 4096),
                   (1, 16640, 4096), (8, 8192, 8192), (7, 14000, 4096)]:
