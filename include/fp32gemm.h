@@ -77,8 +77,8 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
  * weight W = B is K x N, Y = C is M x N; M is the number of sequences
  * decoded at once).  Bandwidth-bound: the time is one pass over W.  The
  * library picks the kernel by shape:
- *  - large W with few 256-column blocks (for example 4096 x 4096 at
- *    M <= 4): K is split across workgroups, each reading 1 KB runs of W's
+ *  - large W with few 256-column blocks (for example 4096 x 4096 at any
+ *    M up to 8): K is split across workgroups, each reading 1 KB runs of W's
  *    rows over a chunk of K; the chunks' partial sums are added in chunk
  *    order by the last workgroup of each column block, in the same kernel.
  *    The partial sums and arrival counters live in device memory the
@@ -246,9 +246,10 @@ int sgemm_splitk_noalloc(int transA, int transB, int M, int N, int K,
  * per workgroup at most) and must not overlap A, B or C or be used by
  * another call until this one has completed on its stream.  Arrival
  * counters live in device memory the library reserves statically per
- * stream (8 streams per device; beyond that they go to the end of the
- * workspace, cleared by a small kernel before the main one).  M <= 8 runs
- * the GEMV kernels as sgemm_ex does and needs no workspace.
+ * stream (8 streams per device, up to 4096 C tiles per call; past either
+ * limit they go to the end of the workspace, cleared by a small kernel
+ * before the main one).  M <= 8 runs the GEMV kernels as sgemm_ex does and
+ * needs no workspace.
  *
  * Argument positions for error codes: transA 1, transB 2, M 3, N 4, K 5,
  * alpha 6, A 7, lda 8, B 9, ldb 10, beta 11, C 12, ldc 13, workspace 14
