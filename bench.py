@@ -201,10 +201,42 @@ def main():
         par = guarded(lambda: full_parity(dC.cpu().numpy(), A, B, C0, w.alpha, w.beta))
         ms = timed(lambda i: check(fg.sgemm(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC,
                                             w.N, sp)), 200, args.small_steps, w.name)
+
+        def graph_rate(calls=100, replays=20):
+            """Microseconds per call with the host out of the loop: `calls`
+            sgemm calls captured in one HIP graph, replayed `replays` times."""
+            def burst(n):
+                for _ in range(n):
+                    check(fg.sgemm(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N,
+                                   None))
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                burst(3)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                burst(calls)
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return round(e0.elapsed_time(e1) / (replays * calls) * 1e3, 3)
+
+        graph_us = guarded(graph_rate)
         configs[w.name] = {"M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
                            "us_per_call": round(ms * 1e3, 3), "bound": "overhead",
                            "note": "back-to-back calls on one stream: launch rate, not the "
                                    "kernel's own duration",
+                           "us_per_call_graph": graph_us,
+                           "graph_note": "100 calls captured in one HIP graph and replayed: the "
+                                         "GPU's rate per call without the host's launch work",
                            "kernel_config": fg.fp32gemm_config_name(
                                fg.KIND_SGEMM, fg.fp32gemm_select_config(fg.KIND_SGEMM, w.M, w.N,
                                                                         w.K)),
