@@ -1,7 +1,8 @@
 """Seeded random cases over every entry point, element by element against the oracle.
 
 Each case draws an entry point (sgemm, sgemv, sgemm_ex, sgemm_strided_batched,
-sgemm_fused, sgemm_splitk, or sgemm / sgemv with a tile or GEMV configuration
+sgemm_fused, sgemm_splitk, sgemm_streamk with the library's plan or a forced
+tile and workgroup count, or sgemm / sgemv with a tile or GEMV configuration
 forced, drawn from all of them), a shape with M from the decode range (1..8, or
 9..128 for the GEMV entry points) or up to a few tiles with ragged tails, operand transposes, padded leading
 dimensions, operands shifted off 16-byte alignment, alpha and beta (zero
@@ -23,8 +24,9 @@ from gpu_util import assert_parity, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-ENTRIES = ("sgemm", "sgemv", "sgemm_ex", "batched", "fused", "splitk", "sgemm_cfg", "sgemv_cfg")
-N_CASES = 432
+ENTRIES = ("sgemm", "sgemv", "sgemm_ex", "batched", "fused", "splitk", "sgemm_cfg", "sgemv_cfg",
+           "streamk")
+N_CASES = 486
 SENTINEL = 12345.0
 
 
@@ -39,7 +41,7 @@ def draw_case(i):
         M = int(g.integers(9, 331))
     N = int(g.integers(1, 331))
     K = int(g.integers(1, 401))
-    trans = entry in ("sgemm_ex", "batched", "fused", "splitk")
+    trans = entry in ("sgemm_ex", "batched", "fused", "splitk", "streamk")
     ta = int(g.integers(0, 2)) if trans else 0
     tb = int(g.integers(0, 2)) if trans else 0
     pads = tuple(int(p) for p in g.integers(0, 6, size=3)) if g.random() < 0.5 else (0, 0, 0)
@@ -59,9 +61,18 @@ def draw_case(i):
         ok = [c for c in range(fg.fp32gemm_num_configs(fg.KIND_SGEMV))
               if fg.fp32gemm_config_max_rows(fg.KIND_SGEMV, c) >= M]
         cfg = ok[int(g.integers(0, len(ok)))]
+    # stream-K: the library's plan, or a forced tile with few workgroups (a
+    # workgroup then spans several tiles and tiles are cut into many segments)
+    sk_tile, sk_groups = -1, 0
+    if entry == "streamk" and g.random() < 0.5:
+        ntiles = 0
+        while fg.fp32gemm_streamk_tile_name(ntiles) is not None:
+            ntiles += 1
+        sk_tile = int(g.integers(0, ntiles))
+        sk_groups = int(g.choice([1, 3, 7, 40, 0]))
     return dict(entry=entry, M=M, N=N, K=K, ta=ta, tb=tb, pads=pads, offset=offset,
                 alpha=alpha, beta=beta, kind=kind, batch=batch, has_bias=has_bias, act=act,
-                splits=splits, cfg=cfg, seed=9000 + i)
+                splits=splits, cfg=cfg, sk_tile=sk_tile, sk_groups=sk_groups, seed=9000 + i)
 
 
 def _draw(g, kind, r, c):
@@ -129,6 +140,18 @@ def run_case(c):
         db = None if bias is None else torch.from_numpy(bias).cuda()
         keep.append(db)
         rc = fg.sgemm_fused(ta, tb, M, N, K, al, pa, lda, pb, ldb, be, pc, ldc, db, c["act"])
+    elif e == "streamk":
+        if c["sk_tile"] < 0:
+            nbytes = fg.sgemm_streamk_workspace_size(M, N, K)
+        else:
+            nbytes = fg.fp32gemm_streamk_plan(M, N, K, c["sk_tile"], c["sk_groups"])[0]
+        ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device="cuda")
+        keep.append(ws)
+        if c["sk_tile"] < 0:
+            rc = fg.sgemm_streamk(ta, tb, M, N, K, al, pa, lda, pb, ldb, be, pc, ldc, ws, nbytes)
+        else:
+            rc = fg.fp32gemm_streamk_with_config(c["sk_tile"], c["sk_groups"], ta, tb, M, N, K, al,
+                                                 pa, lda, pb, ldb, be, pc, ldc, ws, nbytes)
     else:
         nbytes = fg.sgemm_splitk_workspace_size(M, N, K, c["splits"])
         ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device="cuda")
