@@ -15,9 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
-# the HBM streaming probe (measurement only, its own library)
-PROBE_SOURCE = "hbm_probe.hip"
-PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
+# the measurement probes (HBM streaming, matrix-core issue), one library each
+PROBES = {"hbm_probe.hip": os.path.join(HERE, "libhbmprobe.so"),
+          "mfma_probe.hip": os.path.join(HERE, "libmfmaprobe.so")}
 SOURCES = ["api.hip", "dispatch.hip", "sgemm_configs.hip", "sgemm_nn.hip", "sgemm_nt.hip",
            "sgemm_tn.hip", "sgemm_tt.hip", "sgemv.hip", "gemv_split.hip", "skinny.hip",
            "splitk.hip", "streamk.hip"]
@@ -61,10 +61,12 @@ def _link(objs, out):
 
 def build(jobs: int = 8) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
-    _link(objs[-1:], PROBE_LIB)
-    return _link(objs[:-1], LIB)
+    probes = list(PROBES)
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + len(probes))) as ex:
+        objs = list(ex.map(_compile, SOURCES + probes))
+    for src, obj in zip(probes, objs[len(SOURCES):]):
+        _link([obj], PROBES[src])
+    return _link(objs[:len(SOURCES)], LIB)
 
 
 if __name__ == "__main__":
