@@ -414,3 +414,31 @@ def test_stripe_width_by_rounds():
     for M in (65, 100, 128):
         cfg = fg.fp32gemm_select_config(1, M, 16384, 4096)
         assert fg.fp32gemm_config_max_rows(1, cfg) >= M
+
+
+def test_measurement_probes_check_their_arguments():
+    """The two measurement probes (their own libraries, outside the GEMM
+    ABI) load, export one entry point each, and reject shapes their kernels
+    do not take before touching the GPU."""
+    import ctypes
+    from fp32_gemm_06_amd import build
+    for path in build.PROBES.values():
+        if not os.path.exists(path):
+            build.build()
+            break
+    hbm = ctypes.CDLL(build.PROBES["hbm_probe.hip"])
+    hbm.hbm_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    n = 4096 * 4096
+    assert hbm.hbm_stream_read(16, n, 256, 6, 16, None, None) == -1       # waves 4 or 8
+    assert hbm.hbm_stream_read(16, n + 256, 256, 4, 16, None, None) == -1  # whole steps only
+    assert hbm.hbm_stream_read(16, n, 0, 4, 16, None, None) == -1
+    assert hbm.hbm_stream_read(16, 0, 256, 4, 16, None, None) == -1
+    mfma = ctypes.CDLL(build.PROBES["mfma_probe.hip"])
+    mfma.mfma_issue_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    assert mfma.mfma_issue_rate(8, 256, 4, 10, 16, 16, None) == -1   # 32x32x2 or 16x16x4
+    assert mfma.mfma_issue_rate(32, 256, 2, 10, 16, 16, None) == -1  # waves 4 or 8
+    assert mfma.mfma_issue_rate(32, 0, 4, 10, 16, 16, None) == -1
+    assert mfma.mfma_issue_rate(32, 256, 4, 0, 16, 16, None) == -1
+    assert mfma.mfma_issue_rate(32, 256, 4, 10, None, 16, None) == -1
+    assert mfma.mfma_issue_rate(32, 256, 4, 10, 16, None, None) == -1
