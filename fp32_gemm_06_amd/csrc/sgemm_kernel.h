@@ -419,6 +419,58 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m, SkArgs sk) {
         for (int j = 0; j < T::TN; ++j) f.b[j][st] = pb[st * BN + j * 32];
     }
   };
+  // The values one 32 x 32 block takes in the four steps of step group g,
+  // from the positions read_frag reads: block row i of op(A), block column j
+  // of op(B).
+  auto read_a_blk = [&](const float *buf, int g, int i, float(&q)[4]) {
+    if constexpr (KCA) {
+      const float *pa = buf + ar * BK + 4 * ((half * (BK / 8) + g) ^ asw);
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(pa + i * 32 * BK);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) q[st] = v[st];
+    } else {
+      const float *pa = buf + (half * (BK / 2) + 4 * g) * BM + half * 32 + ar;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) q[st] = pa[st * BM + i * 32];
+    }
+  };
+  auto read_b_blk = [&](const float *buf, int g, int j, float(&q)[4]) {
+    const float *Bs = buf + OA::FLOATS;
+    if constexpr (KCB) {
+      const float *pb = Bs + br * BK + 4 * ((half * (BK / 8) + g) ^ bsw);
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(pb + j * 32 * BK);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) q[st] = v[st];
+    } else {
+      const float *pb = Bs + (half * (BK / 2) + 4 * g) * BN + half * 32 + br;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) q[st] = pb[st * BN + j * 32];
+    }
+  };
+  // Epilogue pieces.  Accumulator register v of lane l holds row
+  // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32 x 32 block (16 x 16
+  // blocks: register v of lane (q, c) holds row 4 q + v, column c).
+  auto c_off = [&](int i, int j, int v) -> uint32_t {
+    const int row = MF == 32 ? wm * T::WM + i * 32 + 8 * (v / 4) + 4 * half + (v % 4)
+                             : wm * T::WM + i * 16 + 4 * q4 + v;
+    const int col = wn * T::WN + j * MF + lr;
+    return (row < rows && col < cols) ? (uint32_t)(row * a.ldc + col) * 4u : kOob;
+  };
+  // this lane's bias value per block column (0 without a bias)
+  auto load_bias = [&](float(&bj)[T::TN]) {
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) bj[j] = 0.0f;
+    if (a.bias != nullptr) {
+      const __amdgpu_buffer_rsrc_t rs_bias = make_rsrc(a.bias + n0);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const int col = wn * T::WN + j * MF + lr;
+        const uint32_t off = col < cols ? (uint32_t)col * 4u : kOob;
+        bj[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_bias, off, 0, 0));
+      }
+    }
+  };
+
   auto mma = [&](const Frag &f) {
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -527,9 +579,67 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m, SkArgs sk) {
     __syncthreads();
     if constexpr (SK) signal_pending();
     read_frag(lds, g0, f0);
-    for (int kt = 0; kt < nk; ++kt) {
+    // With one K group and beta = 0, the last slice runs one row of blocks at
+    // a time, and each finished row is scaled and stored while the next
+    // row's MFMAs run: writing C overlaps the last slice instead of following
+    // it.  Every block still takes the slice's steps in the same order.
+    constexpr bool ROWS_LAST = T::KS == 1 && !SK && MF == 32;
+    const bool rows_last = ROWS_LAST && a.beta == 0.0f;
+    const int nreg = rows_last ? nk - 1 : nk;
+    for (int kt = 0; kt < nreg; ++kt) {
       const int c = kt & 1;
       slice(lds + c * STAGE, lds + (c ^ 1) * STAGE, kt);
+    }
+    if constexpr (ROWS_LAST) {
+      if (rows_last) {
+        const float *cur = lds + ((nk - 1) & 1) * STAGE;
+        constexpr int NS = NGW * 4;  // steps of a slice
+        float bq[T::TN][NS];
+#pragma unroll
+        for (int g = 0; g < NGW; ++g)
+#pragma unroll
+          for (int j = 0; j < T::TN; ++j) {
+            float q[4];
+            read_b_blk(cur, g0 + g, j, q);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) bq[j][g * 4 + st] = q[st];
+          }
+        float aq[2][NS];
+        auto read_a_row = [&](int i, float(&r)[NS]) {
+#pragma unroll
+          for (int g = 0; g < NGW; ++g) {
+            float q[4];
+            read_a_blk(cur, g0 + g, i, q);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) r[g * 4 + st] = q[st];
+          }
+        };
+        const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(Cg + (size_t)m0 * a.ldc + n0);
+        float bj[T::TN];
+        load_bias(bj);
+        const bool fused = a.bias != nullptr || a.act != kActNone;
+        read_a_row(0, aq[0]);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+          if (i + 1 < T::TM) read_a_row(i + 1, aq[(i + 1) & 1]);
+#pragma unroll
+          for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(aq[i & 1][st], bq[j][st], acc[i][j],
+                                                              0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < T::ACCN; ++v) {
+              float out = a.alpha * acc[i][j][v];
+              if (fused) out = apply_act(out + bj[j], a.act);
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, out), rs_c, c_off(i, j, v),
+                                                    0, 0);
+            }
+        }
+        return;
+      }
     }
   }
   }  // main loop
@@ -650,31 +760,13 @@ sgemm_kernel(GemmArgs a, int tiles_m, int tiles_n, int group_m, SkArgs sk) {
   }
 
   // ---- epilogue: C = act(alpha * acc + beta * C + bias[col]) ----------------
-  // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32 of its 32 x 32 block.  The bias and the activation are the
-  // fused elementwise chain of "GPU 基础原理", section "4.1 算子融合",
-  // applied in registers before the only store of C.
+  // The bias and the activation are the fused elementwise chain of "GPU 基础
+  // 原理", section "4.1 算子融合", applied in registers before the only store
+  // of C.
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(Cg + (size_t)m0 * a.ldc + n0);
   const float alpha = a.alpha, beta = a.beta;
-  // (16 x 16 blocks: register v of lane (q, c) holds row 4 q + v, column c.)
-  auto c_off = [&](int i, int j, int v) -> uint32_t {
-    const int row = MF == 32 ? wm * T::WM + i * 32 + 8 * (v / 4) + 4 * half + (v % 4)
-                             : wm * T::WM + i * 16 + 4 * q4 + v;
-    const int col = wn * T::WN + j * MF + lr;
-    return (row < rows && col < cols) ? (uint32_t)(row * a.ldc + col) * 4u : kOob;
-  };
-  float bj[T::TN];  // this lane's bias value per 32-column block
-#pragma unroll
-  for (int j = 0; j < T::TN; ++j) bj[j] = 0.0f;
-  if (a.bias != nullptr) {
-    const __amdgpu_buffer_rsrc_t rs_bias = make_rsrc(a.bias + n0);
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-      const int col = wn * T::WN + j * MF + lr;
-      const uint32_t off = col < cols ? (uint32_t)col * 4u : kOob;
-      bj[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_bias, off, 0, 0));
-    }
-  }
+  float bj[T::TN];  // this lane's bias value per block column
+  load_bias(bj);
   const bool fused = a.bias != nullptr || a.act != kActNone;
   const int act = a.act;
   auto finish = [&](float out, int j) -> float { return fused ? apply_act(out + bj[j], act) : out; };
