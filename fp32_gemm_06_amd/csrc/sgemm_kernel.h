@@ -32,7 +32,10 @@
 //  * tiles that overhang M, N or K are zero-filled by buffer loads whose
 //    out-of-range offsets read zero, and stores outside C are dropped the same
 //    way ("GPU 基础原理", section "最后一个考虑：分块的量化"), so interior and
-//    edge tiles run one instruction stream.
+//    edge tiles run one instruction stream;
+//  * with beta = 0 the last K slice finishes one row of blocks at a time and
+//    stores it while the next row's MFMAs run, so writing C overlaps the end
+//    of the K loop instead of following it.
 //
 // Operand layouts.  op(A) is M x K and op(B) is K x N.  An operand is
 // k-contiguous (KC) when its storage rows run along k: A as given, or B when
