@@ -98,3 +98,42 @@ def test_all_ones(shape):
     got, _ = run_hip(inputs.ones(M, K), inputs.ones(K, N), C0, 2.0, 0.5)
     want = np.float64(2.0 * K) + 0.5 * C0.astype(np.float64)
     assert_bitexact(got, want, f"ones {shape}")
+
+
+
+@pytest.mark.parametrize("layout", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=str)
+def test_beta_zero_path_keeps_the_k_order(layout):
+    """With beta = 0 the tiled kernels finish their last K slice one row of
+    blocks at a time and store it at once; with beta != 0 they take the
+    plain epilogue.  Both must sum every element in the same order: on
+    full-mantissa data, C from beta = 0 equals C from beta = 1 over C0 = 0
+    bit for bit (adding beta * 0 is exact).  Every configuration for
+    op(A) op(B) = A B, the library's choice for the transposed layouts; the
+    aligned (128-bit) and the 4-byte aligned (32-bit) operand paths."""
+    torch = require_gpu()
+    ta, tb = layout
+    for (M, N, K, off) in [(300, 520, 260, 0), (129, 67, 97, 1)]:
+        A, B, _ = inputs.random_case(M + N + K + off, M, N, K, kind="uniform")
+        sa = np.ascontiguousarray(A.T) if ta else A
+        sb = np.ascontiguousarray(B.T) if tb else B
+        lda, ldb = (M if ta else K), (K if tb else N)
+        # an offset of one float leaves the operands only 4-byte aligned
+        fa = torch.zeros(sa.size + 4, device="cuda")
+        fa[off:off + sa.size] = torch.from_numpy(sa.reshape(-1)).cuda()
+        fb = torch.zeros(sb.size + 4, device="cuda")
+        fb[off:off + sb.size] = torch.from_numpy(sb.reshape(-1)).cuda()
+        pa, pb = fa.data_ptr() + 4 * off, fb.data_ptr() + 4 * off
+        cfgs = range(fg.fp32gemm_num_configs(0)) if layout == (0, 0) else [None]
+        for cfg in cfgs:
+            outs = []
+            for beta in (0.0, 1.0):
+                C = torch.full((M, N), float("nan") if beta == 0.0 else 0.0, device="cuda")
+                if cfg is None:
+                    rc = fg.sgemm_ex(ta, tb, M, N, K, 1.0, pa, lda, pb, ldb, beta, C, N)
+                else:
+                    rc = fg.fp32gemm_sgemm_with_config(cfg, M, N, K, 1.0, pa, lda, pb, ldb, beta, C, N)
+                assert rc == 0, fg.strerror(rc)
+                outs.append(C)
+            torch.cuda.synchronize()
+            name = "auto" if cfg is None else fg.fp32gemm_config_name(0, cfg)
+            assert torch.equal(outs[0], outs[1]), (layout, (M, N, K, off), name)
