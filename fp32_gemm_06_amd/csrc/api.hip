@@ -128,7 +128,17 @@ int run_tiled(int ta, int tb, const GemmArgs &a, hipStream_t s) {
 // Otherwise the tiled kernel is (N = 11008, M = 64: 79.0 against 86.1 with
 // W stored N x K; M = 96: 132 against 138; N = 8192, M = 128: 79.0 against
 // 90.4).
+// Short K comes first: the skinny kernel's fixed cost (staging X and adding
+// the waves' M x 16 NB partial sums in LDS) grows with the row blocks, and
+// below K = 5 M the tiled kernel's walk over K is the shorter.  Measured over
+// N = 128, 1024 and 4096, both layouts of W, M = 33..128 and K = 128..1024
+// (one GPU, back-to-back calls), the two are level at K = 200-250 for
+// M = 33..48, 320 for M = 64, 640 for M = 128; at K = 128 the tiled kernel
+// takes 5.2-5.7 us against 6.8 (M = 33) to 11.0 (M = 128).  Up to 32 rows
+// (two row blocks) the skinny kernel is the faster at every K (M = 32,
+// K = 128: 4.5 against 5.1 us).
 bool skinny_pays(const GemmArgs &a) {
+  if (a.M > 32 && a.K < 5 * a.M) return false;
   if (a.M <= 48 || (a.M > 64 && a.M <= 80)) return true;
   if (a.M <= 96 && (long long)a.N * a.batch <= 256 * 32) return true;
   const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + 63) / 64) * a.batch;

@@ -4,7 +4,8 @@ bias[j]) against the oracle's sgemm_fused.
 Integer data and integer biases keep every value exact, so these cases are
 bit-exact; uniform data use the standard tolerance with the bias added to the
 scale.  Shapes reach the 64x64, 128x128 and 256x256 tiles, both GEMV kernels
-(M <= 8 with B as given and stored transposed), and the alpha = 0 path.
+(M <= 8 with B as given and stored transposed), the skinny MFMA kernel
+(M = 9..128 with K >= 5 M), and the alpha = 0 path.
 """
 import itertools
 
@@ -53,7 +54,7 @@ def _ints(seed, M, N, K):
 
 
 SHAPES = [(300, 260, 130), (257, 255, 129), (2000, 2000, 64), (4092, 4092, 40), (5, 300, 500),
-          (8, 1000, 777), (1, 64, 33)]
+          (8, 1000, 777), (1, 64, 33), (48, 530, 700), (100, 257, 1001)]
 
 
 @pytest.mark.parametrize("act", [0, 1])

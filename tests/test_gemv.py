@@ -107,9 +107,10 @@ def test_wide_rows_every_config(M):
 @pytest.mark.parametrize("M", [9, 16, 24, 32, 48, 64, 96, 128])
 def test_wide_rows_routed(M):
     """sgemm with M = 9..128 (the skinny kernel where it pays, the tiled
-    kernel where it has 256 tiles or more), and sgemv, against the oracle."""
+    kernel where it has 256 tiles or more or where K < 5 M), and sgemv
+    (always the skinny kernel), against the oracle."""
     require_gpu()
-    for (N, K) in [(4096, 1024), (24576, 256)]:
+    for (N, K) in [(4096, 1024), (24576, 256), (530, 130)]:
         A, B, C0 = inputs.random_case(M + N, M, N, K, kind="uniform")
         ref = oracle.sgemm(A, B, C0, 0.75, -1.0)
         bnd = oracle.bound(A, B, C0, 0.75, -1.0)
@@ -148,11 +149,11 @@ def test_wide_rows_weight_transposed(ta, M):
 
 def test_wide_rows_batched():
     """Strided batches of M = 16, 27, 45 and 70 entries in one skinny grid,
-    both weight layouts."""
+    both weight layouts (K = 700: the skinny kernel's side of K = 5 M)."""
     from test_transpose_batched import _case, run_batched
     for M in (16, 27, 45, 70):
         for tb in (0, 1):
-            As, Bs, Cs = _case(7300 + M, M, 200, 300, batch=3)
+            As, Bs, Cs = _case(7300 + M, M, 200, 700, batch=3)
             outs, ok = run_batched(0, tb, As, Bs, Cs, 1.0, 1.0, pads=(1, 2, 3), gaps=(7, 5, 3))
             assert ok, "write outside C"
             for b in range(3):
@@ -163,12 +164,12 @@ def test_wide_rows_batched():
 @pytest.mark.parametrize("tb", (0, 1))
 @pytest.mark.parametrize("M,offset", [(48, 0), (80, 0), (48, 1), (80, 1)])
 def test_wide_rows_batched_wide_stripes(tb, M, offset):
-    """Four entries of M x 4096 x 300: the grid of 16-column stripes takes four
+    """Four entries of M x 4096 x 700: the grid of 16-column stripes takes four
     rounds, so the skinny kernel runs 64-column stripes (M = 48, W stored
     K x N) or 32-column ones; one float off a 16-byte boundary, the weight is
     read a float at a time (stored N x K) or on 16-column stripes (K x N)."""
     from test_transpose_batched import _case, run_batched
-    As, Bs, Cs = _case(7500 + M + tb + offset, M, 4096, 300, batch=4)
+    As, Bs, Cs = _case(7500 + M + tb + offset, M, 4096, 700, batch=4)
     outs, ok = run_batched(0, tb, As, Bs, Cs, 1.0, 0.5, offset=offset)
     assert ok, "write outside C"
     for b in range(4):
