@@ -126,6 +126,24 @@ int select_gemm_config(int M, int N, int K, int batch) {
         if (id >= 0) return id;
       }
   int best = model_gemm_config(M, N, K, batch, nullptr);
+  // Where the model settles on the 4-wave 64x64 tile, a 96x96 tile (four
+  // waves of 48x48 on 16x16x4 blocks) is taken when its tiles fill one or
+  // two whole rounds of 256 (at least 89% of the last round's slots, at
+  // least 95% of the tile area inside C): with one or two workgroups per CU
+  // a wave's larger tile keeps the matrix cores busier.  Measured against
+  // the best 64x64 form on one GPU: 1536^3 63.4 us against 73.0, 1536 x 1536
+  // x 4096 160.7 against 187.5, 384 x 6144 x 4096 160.5 against 188.3,
+  // 1536 x 3072 x 1536 109.3 against 121.2, 192 x 11008 x 4096 160.2 against
+  // 188.2.  With four rounds (3072^3) it was 1% slower, with half a round
+  // (768 x 1536 x 4096, 1152^3) 19-23% slower.
+  if (best == find_gemm("64x64x32_w32x32_g4") && K >= 256) {
+    const long long t96 = (long long)((M + 95) / 96) * ((N + 95) / 96) * batch;
+    const long long r96 = (t96 + 255) / 256;
+    const double fill = (double)t96 / (256.0 * (double)r96);
+    const double inside = (double)M * (double)N * batch / ((double)t96 * 96.0 * 96.0);
+    const int id = find_gemm("96x96x32_w48x48_m16_g8");
+    if (id >= 0 && r96 <= 2 && fill >= 0.89 && inside >= 0.95) return id;
+  }
   // With at most one 64x64 tile per CU (16 < tiles <= 256) and K long enough,
   // the variant that stages two K slices per barrier keeps two slices of
   // loads in flight instead of one.  Where B comes from HBM (a weight read

@@ -97,7 +97,9 @@ __device__ __forceinline__ int kc_swizzle(int r) {
 }
 
 // One operand tile: `E` rows or columns along m/n (BM for A, BN for B) by BK
-// along k, loaded by `WAVES` waves in whole 1 KB DMA instructions.
+// along k, loaded by `WAVES` waves in whole 1 KB DMA instructions.  Lane l of
+// instruction `inst` moves float4 chunk f = 64 inst + l of the tile, counted
+// along the storage rows (CP chunks a row).
 template <bool KC, int E, int BK, int WAVES>
 struct Operand {
   // LDS floats of the tile
@@ -105,30 +107,31 @@ struct Operand {
   // DMA instructions per wave per slice (one instruction = 64 lanes x 16 bytes)
   static constexpr int NI = E * BK / 256 / WAVES;
   static_assert(E * BK % (256 * WAVES) == 0, "whole DMA instructions per wave");
-  // KC: chunks per row, rows per instruction; MC: chunks per k-row, k-rows per instruction
+  // KC: chunks per row (along k); MC: chunks per k-row (along m / n)
   static constexpr int CP = KC ? BK / 4 : E / 4;
-  static constexpr int RP = 64 / CP;
-  static_assert(64 % CP == 0, "rows per instruction");
-  static_assert(KC || (BK / 2) % RP == 0, "an MC instruction stays inside one k-half");
+  static_assert(!KC || 64 % CP == 0, "a KC instruction covers whole rows");
+  static_assert(KC || (BK / 2) * CP % 64 == 0, "each k-half of an MC tile is whole instructions");
 
-  // LDS float offset where instruction `inst` writes its 1 KB
+  // LDS float offset where instruction `inst` writes its 1 KB (MC: the second
+  // k-half sits 32 floats further on)
   __device__ __forceinline__ static int dst(int inst) {
     if constexpr (KC) return inst * 256;
-    else {
-      const int k = inst * RP;
-      return k * E + (k >= BK / 2 ? 32 : 0);
-    }
+    else return inst * 256 + (inst * 64 >= (BK / 2) * CP ? 32 : 0);
   }
   // Source element (row along storage, column along storage) of the first of
   // the 4 floats this lane moves in instruction `inst`.  KC: (e, k); MC: (k, e).
   __device__ __forceinline__ static void src(int inst, int lane, int &row, int &col) {
-    if constexpr (KC) {
-      row = inst * RP + lane / CP;                          // along m / n
-      col = 4 * ((lane % CP) ^ kc_swizzle<BK>(row));        // along k
+    int c;  // chunk f % CP of the row
+    if constexpr (64 % CP == 0) {
+      row = inst * (64 / CP) + lane / CP;  // whole rows per instruction
+      c = lane % CP;
     } else {
-      row = inst * RP + lane / CP;                          // along k
-      col = (lane % CP) * 4;                                // along m / n
+      const int f = inst * 64 + lane;
+      row = f / CP;
+      c = f % CP;
     }
+    // KC: row along m / n, col along k; MC: row along k, col along m / n
+    col = KC ? 4 * (c ^ kc_swizzle<BK>(row)) : 4 * c;
   }
 };
 
@@ -899,7 +902,8 @@ hipError_t launch_sk(const GemmArgs &a, bool dma, int group_m, int groups, const
   X(64, 64, 32, 32, 32, 1, 4, 1, 32)     \
   X(64, 64, 32, 32, 32, 2, 2, 2, 32)     \
   X(32, 128, 32, 32, 32, 1, 1, 3, 32)    \
-  X(64, 64, 32, 32, 32, 1, 1, 4, 16)
+  X(64, 64, 32, 32, 32, 1, 1, 4, 16)     \
+  X(96, 96, 32, 48, 48, 1, 1, 2, 16)
 // The tiles with a stream-K form (one K group, one slice per barrier); the
 // occupancy column is the stream-K kernel's own (its fix-up needs more
 // registers than the plain kernel: the 128x128 form fits one workgroup per

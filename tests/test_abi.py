@@ -370,6 +370,15 @@ def test_model_choices():
     for shape in [(96, 11008, 4096), (352, 4096, 4096)]:
         assert name(*shape).startswith("64x64x32_w32x32_g"), shape
     assert name(288, 11008, 4096) == "64x64x32_w32x32_m16_g8"
+    # 96x96 tiles where they fill one or two whole rounds of 256 (89% of the
+    # last round's slots, 95% of the tile area inside C), K >= 256
+    for shape in [(1536, 1536, 4096), (384, 6144, 4096), (1536, 3072, 1536), (192, 11008, 4096),
+                  (1530, 1530, 257), (768, 3072, 4096)]:
+        assert name(*shape) == "96x96x32_w48x48_m16_g8", shape
+    # not with half a round, four rounds, padding past C, or short K
+    for shape in [(768, 1536, 4096), (1152, 1152, 1152), (3072, 3072, 3072), (160, 11008, 4096),
+                  (1530, 1530, 100)]:
+        assert not name(*shape).startswith("96x96"), shape
 
 
 def test_split_gemv_choice():

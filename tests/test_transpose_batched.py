@@ -174,6 +174,25 @@ def test_every_config_every_combo():
 
 
 @pytest.mark.parametrize("ta,tb", COMBOS)
+def test_tile96_every_layout(ta, tb):
+    """The 96x96 tile (four waves of 48x48 on 16x16x4 blocks; its k-rows of
+    96 floats are 24 float4 chunks, so one DMA instruction spans parts of
+    three rows) in every operand layout: shapes that fill one round of 256
+    tiles route to it.  Aligned (128-bit DMA path), ragged M, N and K, and
+    operands off a 16-byte boundary (32-bit staged path); bit-exact on
+    integers."""
+    for (M, N, K, pads, offset) in [(1536, 1536, 256, (4, 8, 4), 0), (1530, 1530, 257, (3, 5, 2), 0),
+                                    (1534, 1535, 260, (0, 0, 0), 1)]:
+        assert fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, M, N, K)) == \
+            "96x96x32_w48x48_m16_g8", (M, N, K)
+        As, Bs, Cs = _case(M + N + K + offset + ta + 2 * tb, M, N, K)
+        (got,), ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=pads, offset=offset)
+        assert ok, "write outside C"
+        assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5),
+                        f"96x96 op {ta}{tb} {(M, N, K)} offset {offset}")
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
 def test_batched(ta, tb):
     M, N, K, batch = 100, 132, 70, 5
     As, Bs, Cs = _case(31 + ta + 2 * tb, M, N, K, batch=batch)
