@@ -68,6 +68,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m fp32_gemm_06_amd.build`")
+        # torch brings its own HIP runtime.  Loaded first, it is the one the
+        # library binds to (same soname); loaded after the library, it would
+        # be a second runtime in the process, and whichever of the two opens
+        # the GPU second finds no device.  So torch goes first.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.sgemm.argtypes = _GEMM_ARGTYPES
         L.sgemm.restype = ctypes.c_int

@@ -138,3 +138,33 @@ def test_gemm_wrapper_views_and_epilogue():
                           oracle.sgemm_fused(A, B, C0, 1.0, 0.5, bias, oracle.ACT_RELU))
     with pytest.raises(ValueError):
         fg.gemm(dA, dBt, config=0)
+
+
+def test_host_query_before_torch_import():
+    """A host-only call (the configuration query) made before torch is
+    imported loads the library first.  The binding imports torch before the
+    library, so the process keeps one HIP runtime and the next product still
+    finds the GPU (a second runtime reported no device).  In a fresh process."""
+    import os
+    import subprocess
+    import sys
+    import textwrap
+    require_gpu()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = textwrap.dedent(f"""
+        import sys
+        sys.path.insert(0, {root!r})
+        import fp32_gemm_06_amd as fg
+        assert fg.fp32gemm_select_config(0, 1536, 1536, 256) >= 0
+        import torch
+        A = torch.ones(64, 32, device="cuda")
+        B = torch.ones(32, 48, device="cuda")
+        C = torch.zeros(64, 48, device="cuda")
+        rc = fg.sgemm(64, 48, 32, 1.0, A, 32, B, 48, 0.0, C, 48)
+        torch.cuda.synchronize()
+        assert rc == 0, fg.strerror(rc)
+        assert bool((C == 32).all())
+        print("product ok")
+    """)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "product ok" in r.stdout, r.stdout + r.stderr

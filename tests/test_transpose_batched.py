@@ -202,6 +202,19 @@ def test_batched(ta, tb):
         assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5), f"entry {b}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1)])
+def test_batched_rounds_of_96x96_tiles(ta, tb):
+    """Two entries of 768 x 1536 x 260: 256 tiles of 96x96 over the batch, one
+    round, a shape the library runs on that tile; the entries come from
+    blockIdx.y and their tiles must not overlap."""
+    M, N, K, batch = 768, 1536, 260, 2
+    As, Bs, Cs = _case(41 + ta, M, N, K, batch=batch)
+    outs, ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=(4, 4, 4), gaps=(4, 8, 4))
+    assert ok, "write outside the C entries"
+    for b in range(batch):
+        assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5), f"entry {b}")
+
+
 def test_batched_shared_a_misaligned_strides():
     """strideA = 0 (one A for every entry); odd strides force the 32-bit path."""
     M, N, K, batch = 64, 96, 33, 4
