@@ -89,6 +89,17 @@ def test_bitexact(ta, tb, shape, splits):
     assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"op {ta}{tb} {shape} splits={splits}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1)])
+def test_chunks_on_96x96_tiles(ta, tb):
+    """Two chunks of 768 x 1536 x 520 fill one round of 256 96x96 tiles: the
+    chunk grid runs on that tile (ragged last chunk of K)."""
+    M, N, K = 768, 1536, 1030
+    A, B, C0 = _ints(31 + ta, M, N, K)
+    got, ok, chunks = run_splitk(ta, tb, A, B, C0, 1.0, 0.5, 2, pads=(4, 4, 4))
+    assert chunks == 2 and ok
+    assert_bitexact(got, oracle.sgemm(A, B, C0, 1.0, 0.5), f"op {ta}{tb} 96x96 chunks")
+
+
 @pytest.mark.parametrize("offset,ws_offset", [(1, 0), (0, 1), (3, 2)])
 def test_scalar_paths(offset, ws_offset):
     """Misaligned operands (32-bit tile loads) and a misaligned workspace or
