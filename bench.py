@@ -300,6 +300,8 @@ def main():
                 "weight_stored_KxN": dict(bw(kn_ms), call="sgemv",
                                           kernel_config=fg.fp32gemm_config_name(fg.KIND_SGEMV,
                                                                                 gcfg),
+                                          traffic=stored_traffic(f"gemv_m{m}_4096",
+                                                                 GEMV_SOURCES),
                                           parity=par_kn),
                 "weight_stored_NxK": dict(bw(nk_ms), call="sgemm_ex(transA=0, transB=1)",
                                           parity=par_nk),
