@@ -193,6 +193,23 @@ def test_tile96_every_layout(ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", COMBOS)
+def test_tile16x16_every_layout(ta, tb):
+    """The 64x64 tile on 16x16x4 blocks in every operand layout: its
+    mn-contiguous operand tiles hold their 16-float groups permuted per
+    k-quarter (DMA and 32-bit staged paths alike).  Aligned, ragged M, N and K,
+    and operands off a 16-byte boundary; bit-exact on integers."""
+    for (M, N, K, pads, offset) in [(1024, 2048, 128, (4, 8, 4), 0), (1500, 1400, 130, (3, 5, 2), 0),
+                                    (1401, 1503, 97, (0, 0, 0), 1)]:
+        assert fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, M, N, K)) == \
+            "64x64x32_w32x32_m16_g8", (M, N, K)
+        As, Bs, Cs = _case(M + N + K + offset + 3 * ta + 5 * tb, M, N, K)
+        (got,), ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=pads, offset=offset)
+        assert ok, "write outside C"
+        assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5),
+                        f"16x16 blocks op {ta}{tb} {(M, N, K)} offset {offset}")
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
 def test_batched(ta, tb):
     M, N, K, batch = 100, 132, 70, 5
     As, Bs, Cs = _case(31 + ta + 2 * tb, M, N, K, batch=batch)
