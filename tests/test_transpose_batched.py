@@ -194,10 +194,10 @@ def test_tile96_every_layout(ta, tb):
 
 @pytest.mark.parametrize("ta,tb", COMBOS)
 def test_tile16x16_every_layout(ta, tb):
-    """The 64x64 tile on 16x16x4 blocks in every operand layout: its
-    mn-contiguous operand tiles hold their 16-float groups permuted per
-    k-quarter (DMA and 32-bit staged paths alike).  Aligned, ragged M, N and K,
-    and operands off a 16-byte boundary; bit-exact on integers."""
+    """The 64x64 tile on 16x16x4 blocks in every operand layout (its lane
+    quarters read k-rows from both k-halves of an mn-contiguous tile), through
+    shapes the library runs on it.  Aligned, ragged M, N and K, and operands
+    off a 16-byte boundary (32-bit staged path); bit-exact on integers."""
     for (M, N, K, pads, offset) in [(1024, 2048, 128, (4, 8, 4), 0), (1500, 1400, 130, (3, 5, 2), 0),
                                     (1401, 1503, 97, (0, 0, 0), 1)]:
         assert fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, M, N, K)) == \
