@@ -8,10 +8,11 @@
 // configuration per measured shape; other shapes fall back to a cost model
 // over the same configurations.
 #include <math.h>
-#include <string.h>
 
 #include <mutex>
 #include <string>
+#include <string_view>
+#include <unordered_map>
 #include <vector>
 
 #include "common.h"
@@ -25,8 +26,11 @@ struct ShapeEntry {
 };
 #include "tune_table.inc"
 
+// Configuration names and their ids, built once; the selection runs on every
+// call, so names are looked up by hash, not by scanning the list.
 std::once_flag g_names_once;
 std::vector<std::string> g_gemm_names;
+std::unordered_map<std::string_view, int> g_gemm_ids, g_gemv_ids;
 
 void build_names() {
   int n = 0;
@@ -34,21 +38,21 @@ void build_names() {
   for (int t = 0; t < n; ++t)
     for (int g = 0; g < kNumGroups; ++g)
       g_gemm_names.push_back(std::string(cfg[t].name) + "_g" + std::to_string(kGroups[g]));
+  for (size_t i = 0; i < g_gemm_names.size(); ++i) g_gemm_ids.emplace(g_gemm_names[i], (int)i);
+  const GemvConfig *gv = gemv_configs(&n);
+  for (int i = 0; i < n; ++i) g_gemv_ids.emplace(gv[i].name, i);
 }
 
 int find_gemm(const char *name) {
   std::call_once(g_names_once, build_names);
-  for (size_t i = 0; i < g_gemm_names.size(); ++i)
-    if (g_gemm_names[i] == name) return (int)i;
-  return -1;
+  const auto it = g_gemm_ids.find(name);
+  return it == g_gemm_ids.end() ? -1 : it->second;
 }
 
 int find_gemv(const char *name) {
-  int n = 0;
-  const GemvConfig *cfg = gemv_configs(&n);
-  for (int i = 0; i < n; ++i)
-    if (strcmp(cfg[i].name, name) == 0) return i;
-  return -1;
+  std::call_once(g_names_once, build_names);
+  const auto it = g_gemv_ids.find(name);
+  return it == g_gemv_ids.end() ? -1 : it->second;
 }
 
 }  // namespace
