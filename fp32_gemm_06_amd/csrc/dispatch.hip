@@ -148,6 +148,23 @@ int select_gemm_config(int M, int N, int K, int batch) {
     const int id = find_gemm("96x96x32_w48x48_m16_g8");
     if (id >= 0 && r96 <= 2 && fill >= 0.89 && inside >= 0.95) return id;
   }
+  const double tiles64 = (double)((M + 63) / 64) * (double)((N + 63) / 64) * batch;
+  // With fewer than 192 tiles of 64x64 most CUs would hold none or one
+  // workgroup.  32x32 tiles (four waves of one 16x16x4 block each) give four
+  // times as many workgroups.  With at most two rounds of them and a long K,
+  // four K slices go in flight per stage; otherwise two (less LDS, more
+  // workgroups per CU, a shorter pipeline to fill).  Measured against the
+  // best 64x64 form on one GPU: 384^3 5.5 against 10.0 us, 512^3 6.5 against
+  // 12.3, 768^3 15.0 against 17.0, 800^3 16.0 against 17.9, 512 x 512 x 8192
+  // 59.9 against 141.6, 256 x 1024 x 4096 32.2 against 72.8, 64 x 11008 x
+  // 4096 65.5 against 74.1; at 850^3 and 896^3 (196 tiles) they were within
+  // 2% either way.
+  if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 < 192.0 && K >= 128) {
+    const double t32 = (double)((M + 31) / 32) * (double)((N + 31) / 32) * batch;
+    const bool deep = t32 <= 512.0 && K >= 1024;
+    const int id = find_gemm(deep ? "32x32x32_w16x16_p4_m16_g8" : "32x32x32_w16x16_p2_m16_g8");
+    if (id >= 0) return id;
+  }
   // With at most one 64x64 tile per CU (16 < tiles <= 256) and K long enough,
   // the variant that stages two K slices per barrier keeps two slices of
   // loads in flight instead of one.  Where B comes from HBM (a weight read
@@ -158,7 +175,6 @@ int select_gemm_config(int M, int N, int K, int batch) {
   // two groups of waves times the same with B cached but 8-13% slower from
   // HBM.  At 320..512 tiles the plain tile is up to 3% faster, and with
   // K = 260 the staging covers too few slices.
-  const double tiles64 = (double)((M + 63) / 64) * (double)((N + 63) / 64) * batch;
   if (best == find_gemm("64x64x32_w32x32_g4") && tiles64 > 16.0 && tiles64 <= 256.0 && K >= 512) {
     const int p2 = find_gemm("64x64x32_w32x32_p2_g8");
     if (p2 >= 0) best = p2;

@@ -903,7 +903,10 @@ hipError_t launch_sk(const GemmArgs &a, bool dma, int group_m, int groups, const
   X(64, 64, 32, 32, 32, 2, 2, 2, 32)     \
   X(32, 128, 32, 32, 32, 1, 1, 3, 32)    \
   X(64, 64, 32, 32, 32, 1, 1, 4, 16)     \
-  X(96, 96, 32, 48, 48, 1, 1, 2, 16)
+  X(96, 96, 32, 48, 48, 1, 1, 2, 16)     \
+  X(32, 32, 32, 16, 16, 1, 2, 4, 16)     \
+  X(32, 32, 32, 16, 16, 1, 4, 2, 16)     \
+  X(64, 32, 32, 32, 16, 1, 2, 3, 16)
 // The tiles with a stream-K form (one K group, one slice per barrier); the
 // occupancy column is the stream-K kernel's own (its fix-up needs more
 // registers than the plain kernel: the 128x128 form fits one workgroup per

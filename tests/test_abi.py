@@ -347,20 +347,27 @@ def test_round_split_plan():
 def test_model_choices():
     """The fallback tile model on shapes the table does not list: short K
     moves large products from 256x256 to 128x128 tiles (each tile's fixed
-    cost is a larger share), at most one 64x64 tile per CU takes the variant
-    with two K slices per barrier (K >= 512 only), more tiles keep the plain
-    64x64 tile, and a K too short to stage keeps it too."""
+    cost is a larger share), fewer than 192 tiles of 64x64 go to 32x32 tiles,
+    192..256 of them take the variant with two K slices per barrier (K >= 512
+    only), more tiles keep the plain 64x64 tile, and a K too short to stage
+    keeps it too."""
     name = lambda *s: fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, *s))
     assert name(8192, 4096, 4096).startswith("256x256x32_")
     assert name(8192, 4096, 128).startswith("128x128x32_w64x32")
     assert name(4096, 4096, 64).startswith("128x128x32_w64x32")
-    for shape in [(160, 4096, 4096), (192, 4096, 4096), (256, 4096, 11008), (1000, 1000, 1000),
-                  (200, 2000, 8000)]:
+    for shape in [(160, 4096, 4096), (192, 4096, 4096), (256, 4096, 11008), (1000, 1000, 1000)]:
         assert name(*shape) == "64x64x32_w32x32_p2_g8", shape
-    for shape in [(384, 4096, 4096), (320, 4096, 4096), (1100, 1100, 1100), (300, 520, 260)]:
+    for shape in [(384, 4096, 4096), (320, 4096, 4096), (1100, 1100, 1100)]:
         assert name(*shape).startswith("64x64x32_w32x32_g"), shape
-    # tiny products keep the plain tile: 2 x 2 tiles
-    assert name(100, 100, 4096).startswith("64x64x32_w32x32_g")
+    # 32x32 tiles below 192 tiles of 64x64 (K >= 128): four K slices per
+    # stage with at most 512 of them and K >= 1024, two otherwise
+    for shape in [(200, 2000, 8000), (100, 100, 4096), (512, 512, 8192), (256, 1024, 4096)]:
+        assert name(*shape) == "32x32x32_w16x16_p4_m16_g8", shape
+    for shape in [(300, 520, 260), (800, 800, 800), (64, 11008, 4096), (1000, 700, 300),
+                  (700, 700, 700)]:
+        assert name(*shape) == "32x32x32_w16x16_p2_m16_g8", shape
+    for shape in [(896, 896, 896), (850, 850, 850), (512, 512, 100)]:
+        assert not name(*shape).startswith("32x32"), shape
     # 32-row tiles where they save a round of 256 tiles (516 -> 430), not
     # where the rounds stay the same
     assert name(160, 11008, 4096) == "32x128x32_w32x32_g8"

@@ -210,6 +210,37 @@ def test_tile16x16_every_layout(ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", COMBOS)
+def test_tile32x32_every_layout(ta, tb):
+    """The 32x32 tiles (four waves of one 16x16x4 block each) in every operand
+    layout, through shapes the library runs on them: four K slices per stage
+    (aligned, and ragged K past a stage), two (ragged M, N, K), and operands
+    off a 16-byte boundary (32-bit staged path); bit-exact on integers."""
+    for (M, N, K, pads, offset, cfg) in [(256, 512, 1024, (4, 8, 4), 0, "32x32x32_w16x16_p4_m16_g8"),
+                                         (200, 300, 1100, (0, 4, 0), 0, "32x32x32_w16x16_p4_m16_g8"),
+                                         (333, 517, 261, (3, 5, 2), 0, "32x32x32_w16x16_p2_m16_g8"),
+                                         (301, 203, 157, (0, 0, 0), 1, "32x32x32_w16x16_p2_m16_g8")]:
+        assert fg.fp32gemm_config_name(0, fg.fp32gemm_select_config(0, M, N, K)) == cfg, (M, N, K)
+        As, Bs, Cs = _case(M + N + K + offset + 3 * ta + 5 * tb, M, N, K)
+        (got,), ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=pads, offset=offset)
+        assert ok, "write outside C"
+        assert_bitexact(got, oracle.sgemm(As[0], Bs[0], Cs[0], 1.0, 0.5),
+                        f"32x32 tile op {ta}{tb} {(M, N, K)} offset {offset}")
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1)])
+def test_batched_32x32_tiles(ta, tb):
+    """Eight entries of 192 x 160 x 300: 48 tiles of 64x64 over the batch, so
+    the batch runs on 240 tiles of 32x32; the entries come from blockIdx.y and
+    their tiles must not overlap."""
+    M, N, K, batch = 192, 160, 300, 8
+    As, Bs, Cs = _case(43 + ta, M, N, K, batch=batch)
+    outs, ok = run_batched(ta, tb, As, Bs, Cs, 1.0, 0.5, pads=(4, 4, 4), gaps=(4, 8, 4))
+    assert ok, "write outside the C entries"
+    for b in range(batch):
+        assert_bitexact(outs[b], oracle.sgemm(As[b], Bs[b], Cs[b], 1.0, 0.5), f"entry {b}")
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
 def test_batched(ta, tb):
     M, N, K, batch = 100, 132, 70, 5
     As, Bs, Cs = _case(31 + ta + 2 * tb, M, N, K, batch=batch)
